@@ -1,0 +1,402 @@
+"""Pin checks for the CPU oracle, parametrised over an oracle namespace.
+
+Each ``check_*`` function raises AssertionError when the oracle it is given
+disagrees with what the pages or the mathematics fix.  ``test_oracle_pins``
+runs them on the real oracle (all must pass) and on deliberately broken copies
+of it (each copy must fail at least one check), so the checks are shown to
+catch the mistakes they are meant to catch.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+import types
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+from torch.nn.attention.bias import causal_lower_right
+
+import oracle as _oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def real_oracle():
+    return types.SimpleNamespace(
+        decode=_oracle.decode, prefill=_oracle.prefill, slot_mapping=_oracle.slot_mapping,
+        store_kv=_oracle.store_kv, decode_partials=_oracle.decode_partials,
+        lse_merge=_oracle.lse_merge, gather_rows=_oracle.gather_rows,
+        to_f64=_oracle.to_f64)
+
+
+# ---------------------------------------------------------------------------
+# building paged inputs from contiguous float32 K/V with the oracle's own
+# slot_mapping + store_kv (both pinned separately by check_slot_* / check_store)
+
+
+def paged(ns, K, V, block_size, rng, num_blocks=None, maxb=None):
+    """Scatter contiguous per-sequence K/V ``list of [L, HKV, D] float32`` into a pool.
+
+    Returns ``(k_pool, v_pool, block_table, lens)``; the pool holds NaN
+    everywhere a live row is not.
+    """
+    lens = np.array([k.shape[0] for k in K], dtype=np.int32)
+    nblk = [-(-int(L) // block_size) for L in lens]
+    if num_blocks is None:
+        num_blocks = max(1, sum(nblk) + 3)
+    if maxb is None:
+        maxb = max([1] + nblk)
+    HKV, D = K[0].shape[1], K[0].shape[2]
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((len(K), maxb), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    k_pool = np.full((num_blocks, block_size, HKV, D), np.nan, dtype=np.float32)
+    v_pool = np.full_like(k_pool, np.nan)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = ns.slot_mapping(bt, cu, lens, block_size)
+    ns.store_kv(k_pool, v_pool, np.concatenate(K), np.concatenate(V), slots)
+    return k_pool, v_pool, bt, lens
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# slot mapping
+
+
+def check_slot_teaching(ns):
+    g = golden("slot_examples.json")["lab_b2_3_teaching"]
+    bs, bt = g["block_size"], np.array([g["block_table"]], dtype=np.int32)
+    for p, want in zip(g["positions"], g["slots"]):
+        # one new token at position p: a sequence of p+1 keys whose last token is new
+        got = ns.slot_mapping(bt, np.array([0, 1]), np.array([p + 1]), bs)
+        assert got.tolist() == [want], (p, got, want)
+
+
+def check_slot_boundaries(ns):
+    g = golden("slot_examples.json")["lab_b2_3_boundaries"]
+    bs = g["block_size"]
+    for L, nb in zip(g["lengths"], g["blocks"]):
+        # with only the first nb blocks mapped, every one of the L tokens has a slot
+        bt = np.full((1, 4), -1, dtype=np.int32)
+        bt[0, :nb] = np.arange(nb) + 7
+        s = ns.slot_mapping(bt, np.array([0, L]), np.array([L]), bs)
+        assert np.all(s >= 0), (L, nb)
+        if nb > 1:  # one block fewer leaves the tail unmapped
+            bt2 = bt.copy()
+            bt2[0, nb - 1] = -1
+            s2 = ns.slot_mapping(bt2, np.array([0, L]), np.array([L]), bs)
+            assert np.any(s2 == -1)
+
+
+def check_slot_prefill_log(ns):
+    g = golden("slot_examples.json")["kvblog_3_5_prefill"]
+    bt = np.array(g["block_table"], dtype=np.int32)
+    lens = np.array(g["seq_lens_k"], dtype=np.int32)
+    new = lens - np.array(g["num_cached"])
+    cu_q = np.concatenate([[0], np.cumsum(new)])
+    assert cu_q.tolist() == g["cu_seqlens_q"]
+    assert np.concatenate([[0], np.cumsum(lens)]).tolist() == g["cu_seqlens_k"]
+    s = ns.slot_mapping(bt, cu_q, lens, g["block_size"])
+    for b in range(2):
+        sb = s[cu_q[b]:cu_q[b + 1]]
+        assert len(sb) == g["slot_len"][b]
+        assert sb[:10].tolist() == g["slot_first10"][b], (b, sb[:10])
+        assert int(sb[-1]) == g["slot_last"][b]
+
+
+def check_slot_decode_log(ns):
+    g = golden("slot_examples.json")["kvblog_4_4_decode"]
+    bt = np.array(g["block_table"], dtype=np.int32)
+    ctx = np.array(g["context_lens"], dtype=np.int32)
+    s = ns.slot_mapping(bt, np.arange(3), ctx, g["block_size"])
+    assert s.tolist() == g["slot_mapping"], s
+
+
+def check_positions(ns):
+    """Positions of new tokens (slot = position under an identity block table)."""
+    sx = golden("slot_examples.json")
+    ident = np.arange(8, dtype=np.int32)[None, :].repeat(2, 0)
+    bs = 256
+    g = sx["lab_b3_lifecycle"]
+    ctx = np.array(g["decode_context_lens"])
+    assert ns.slot_mapping(ident, np.arange(3), ctx, bs).tolist() == g["decode_positions"]
+    g = sx["lab_b6_prefix"]
+    lk = np.diff(g["cu_seqlens_k"])
+    s = ns.slot_mapping(ident[:1], np.array(g["cu_seqlens_q"]), lk, bs)
+    assert int(s[0]) == g["first_position"] and len(s) == 108
+    g = sx["lab_b2_2_chunk"]
+    cu_q = np.array(g["cu_seqlens_q"])
+    s = ns.slot_mapping(ident, cu_q, np.diff(g["cu_seqlens_k"]), bs)
+    assert [int(s[cu_q[0]]), int(s[cu_q[1]])] == g["first_positions"]
+
+
+# ---------------------------------------------------------------------------
+# store
+
+
+def check_store(ns):
+    rng = np.random.default_rng(5)
+    NB, BS, HKV, D, N = 6, 4, 2, 8, 9
+    kp = np.full((NB, BS, HKV, D), np.nan, dtype=np.float32)
+    vp = kp.copy()
+    slots = rng.permutation(NB * BS)[:N].astype(np.int32)
+    slots[3] = -1
+    key, val = _rand(rng, N, HKV, D), _rand(rng, N, HKV, D)
+    ns.store_kv(kp, vp, key, val, slots)
+    flat_k, flat_v = kp.reshape(NB * BS, HKV, D), vp.reshape(NB * BS, HKV, D)
+    live = slots != -1
+    assert np.array_equal(flat_k[slots[live]], key[live])
+    assert np.array_equal(flat_v[slots[live]], val[live])
+    untouched = np.setdiff1d(np.arange(NB * BS), slots[live])
+    assert np.all(np.isnan(flat_k[untouched])) and np.all(np.isnan(flat_v[untouched]))
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+
+def _decode_contig(ns, q, K, V, scale, bs, rng):
+    """Run ns.decode on contiguous per-sequence K/V via a paged pool."""
+    kp, vp, bt, lens = paged(ns, K, V, bs, rng)
+    return ns.decode(q, kp, vp, bt, lens, scale, "f32")
+
+
+def check_softmax_example(ns):
+    g = golden("lab_b1_attention.json")["softmax_example"]
+    s = np.array(g["scores"])
+    # q = e1, k_j = s_j e1 and one-hot V rows: the output is the weight vector
+    D = 3
+    q = np.zeros((1, 1, D), np.float32); q[0, 0, 0] = 1
+    K = np.zeros((3, 1, D), np.float32); K[:, 0, 0] = s
+    V = np.eye(3, dtype=np.float32)[:, None, :]
+    out = _decode_contig(ns, q, [K], [V], 1.0, 2, np.random.default_rng(0))
+    assert np.allclose(out[0, 0], g["probabilities"], atol=g["abs_tol"], rtol=0), out
+
+
+def check_hand_example(ns):
+    g = golden("lab_b1_attention.json")["hand_example_v_differs"]
+    D = 3
+    q = np.zeros((1, 2, D), np.float32)
+    q[0, :, :2] = g["q"][-1]
+    K = np.zeros((3, 1, D), np.float32); K[:, 0, :2] = g["k"]
+    V = np.zeros((3, 1, D), np.float32); V[:, 0, :2] = g["v"]
+    V1h = np.eye(3, dtype=np.float32)[:, None, :]
+    # head 0 sees V, head 1 (same KV head) -- run twice to get output and weights
+    o = _decode_contig(ns, q, [K], [V], g["scale"], 2, np.random.default_rng(1))
+    w = _decode_contig(ns, q, [K], [V1h], g["scale"], 2, np.random.default_rng(2))
+    tol = g["abs_tol"]
+    assert np.allclose(o[0, 0, :2], g["last_output"], atol=tol, rtol=0), o[0, 0]
+    assert np.allclose(o[0, 1, :2], g["last_output"], atol=tol, rtol=0)
+    assert np.allclose(w[0, 0], g["last_weights"], atol=tol, rtol=0), w[0, 0]
+
+
+def check_cached_append(ns):
+    g = golden("lab_b1_attention.json")
+    x = np.array(g["causal_qkv_equal"]["x"])
+    y = np.vstack([x, [g["cached_append"]["appended_reading"]]]).astype(np.float32)
+    q = y[-1][None, None, :]
+    out = _decode_contig(ns, q, [y[:, None, :]], [y[:, None, :]],
+                         g["causal_qkv_equal"]["scale"], 2, np.random.default_rng(3))
+    c = g["cached_append"]
+    assert np.allclose(out[0, 0], c["last_output"], atol=c["abs_tol"], rtol=0), out
+
+
+def _sdpa_decode(q, K, V, scale, HQ):
+    """torch float64 SDPA on contiguous K/V, KV heads repeated to HQ (GQA)."""
+    outs = []
+    for b in range(len(K)):
+        G = HQ // K[b].shape[1]
+        k = torch.from_numpy(K[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        v = torch.from_numpy(V[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        qq = torch.from_numpy(q[b].astype(np.float64))[:, None, :]
+        outs.append(F.scaled_dot_product_attention(qq, k, v, scale=scale)[:, 0, :].numpy())
+    return np.stack(outs)
+
+
+def check_decode_vs_sdpa(ns):
+    rng = np.random.default_rng(11)
+    for (HQ, HKV, D, bs, lens) in [
+        (2, 1, 8, 4, [1, 3, 4, 5, 9]),
+        (8, 2, 16, 16, [15, 16, 17, 33]),
+        (6, 3, 4, 8, [7, 8, 9, 24]),
+        (4, 4, 8, 2, [1, 2, 3]),
+    ]:
+        K = [_rand(rng, L, HKV, D) for L in lens]
+        V = [_rand(rng, L, HKV, D) for L in lens]
+        q = _rand(rng, len(lens), HQ, D)
+        scale = 1.0 / math.sqrt(D)
+        got = _decode_contig(ns, q, K, V, scale, bs, rng)
+        want = _sdpa_decode(q, K, V, scale, HQ)
+        assert np.allclose(got, want, atol=1e-12, rtol=0), np.abs(got - want).max()
+
+
+def check_block_permutation(ns):
+    rng = np.random.default_rng(12)
+    lens = [5, 17, 40]
+    K = [_rand(rng, L, 2, 8) for L in lens]
+    V = [_rand(rng, L, 2, 8) for L in lens]
+    q = _rand(rng, 3, 4, 8)
+    a = _decode_contig(ns, q, K, V, 0.3, 4, np.random.default_rng(100))
+    b = _decode_contig(ns, q, K, V, 0.3, 4, np.random.default_rng(200))
+    assert np.array_equal(a, b)
+
+
+def check_single_key(ns):
+    rng = np.random.default_rng(13)
+    K, V = [_rand(rng, 1, 2, 8)], [_rand(rng, 1, 2, 8)]
+    q = _rand(rng, 1, 4, 8)
+    out = _decode_contig(ns, q, K, V, 0.5, 4, rng)
+    assert np.array_equal(out[0], np.repeat(V[0][0].astype(np.float64), 2, axis=0))
+
+
+def check_gqa_is_repeat(ns):
+    rng = np.random.default_rng(14)
+    lens = [9, 20]
+    K = [_rand(rng, L, 2, 8) for L in lens]
+    V = [_rand(rng, L, 2, 8) for L in lens]
+    q = _rand(rng, 2, 6, 8)
+    a = _decode_contig(ns, q, K, V, 0.4, 4, rng)
+    Kr = [np.repeat(k, 3, axis=1) for k in K]
+    Vr = [np.repeat(v, 3, axis=1) for v in V]
+    b = _decode_contig(ns, q, Kr, Vr, 0.4, 4, rng)
+    assert np.allclose(a, b, atol=1e-14, rtol=0)
+
+
+def check_empty_context(ns):
+    rng = np.random.default_rng(15)
+    K, V = [_rand(rng, 6, 1, 4)], [_rand(rng, 6, 1, 4)]
+    kp, vp, bt, _ = paged(ns, K, V, 4, rng)
+    q = _rand(rng, 2, 2, 4)
+    bt2 = np.vstack([bt, np.full_like(bt, -1)])
+    out = ns.decode(q, kp, vp, bt2, np.array([6, 0]), 0.5, "f32")
+    assert np.array_equal(out[1], np.zeros((2, 4)))
+    assert np.all(np.isfinite(out[0]))
+
+
+def check_partials_merge(ns):
+    rng = np.random.default_rng(16)
+    lens = [1, 7, 16, 50]
+    K = [_rand(rng, L, 2, 8) for L in lens]
+    V = [_rand(rng, L, 2, 8) for L in lens]
+    q = _rand(rng, 4, 4, 8)
+    kp, vp, bt, ln = paged(ns, K, V, 4, rng)
+    ref = ns.decode(q, kp, vp, bt, ln, 0.35, "f32")
+    for P in (1, 3, 4, 16, 50, 64):
+        NP = -(-max(lens) // P)
+        acc, m, l = ns.decode_partials(q, kp, vp, bt, ln, 0.35, "f32", P, NP)
+        nv = np.array([-(-L // P) for L in lens])
+        got = ns.lse_merge(acc, m, l, nv)
+        assert np.allclose(got, ref, atol=1e-13, rtol=0), (P, np.abs(got - ref).max())
+    # one partition covering everything: acc / l is the output itself
+    acc, m, l = ns.decode_partials(q, kp, vp, bt, ln, 0.35, "f32", 64, 1)
+    assert np.allclose(acc[:, :, 0] / l[:, :, 0, None], ref, atol=1e-14, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+
+
+def _prefill_contig(ns, Q, K, V, lq, scale, bs, rng, causal=True):
+    kp, vp, bt, lens = paged(ns, K, V, bs, rng)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return ns.prefill(np.concatenate(Q), kp, vp, bt, cu_q, cu_k, scale, "f32", causal), cu_q
+
+
+def check_causal_matrix(ns):
+    g = golden("lab_b1_attention.json")["causal_qkv_equal"]
+    x = np.array(g["x"], dtype=np.float32)
+    D = 3
+    X3 = np.zeros((3, 1, D), np.float32); X3[:, 0, :2] = x
+    I3 = np.eye(3, dtype=np.float32)[:, None, :]
+    w, _ = _prefill_contig(ns, [X3], [X3], [I3], [3], g["scale"], 2, np.random.default_rng(4))
+    o, _ = _prefill_contig(ns, [X3], [X3], [X3], [3], g["scale"], 2, np.random.default_rng(5))
+    assert np.allclose(w[:, 0, :], g["weights"], atol=g["abs_tol"], rtol=0), w[:, 0]
+    assert np.allclose(o[-1, 0, :2], g["last_output"], atol=g["abs_tol"], rtol=0)
+
+
+def check_future_change(ns):
+    g = golden("lab_b1_attention.json")
+    x = np.array(g["causal_qkv_equal"]["x"], dtype=np.float32)
+    fc = g["future_change"]
+    y = x.copy(); y[-1] = fc["changed_last"]
+    sc = g["causal_qkv_equal"]["scale"]
+    r = np.random.default_rng(6)
+    for causal, want in ((True, fc["masked_earlier_delta"]), (False, fc["unmasked_earlier_delta"])):
+        a, _ = _prefill_contig(ns, [x[:, None]], [x[:, None]], [x[:, None]], [3], sc, 2, r, causal)
+        b, _ = _prefill_contig(ns, [y[:, None]], [y[:, None]], [y[:, None]], [3], sc, 2, r, causal)
+        delta = np.abs(a[:2] - b[:2]).max()
+        if causal:
+            assert delta == 0.0
+        else:
+            assert abs(delta - want) < fc["abs_tol"], delta
+
+
+def check_prefill_vs_sdpa(ns):
+    rng = np.random.default_rng(17)
+    for (HQ, HKV, D, bs, lk, lq, causal) in [
+        (2, 1, 8, 4, [5, 9, 16], [5, 3, 1], True),
+        (4, 2, 16, 8, [33, 20], [10, 20], True),
+        (6, 2, 8, 16, [40, 7], [17, 7], False),
+    ]:
+        K = [_rand(rng, L, HKV, D) for L in lk]
+        V = [_rand(rng, L, HKV, D) for L in lk]
+        Q = [_rand(rng, n, HQ, D) for n in lq]
+        scale = 0.25
+        got, cu_q = _prefill_contig(ns, Q, K, V, lq, scale, bs, rng, causal)
+        for b in range(len(lk)):
+            G = HQ // HKV
+            qq = torch.from_numpy(Q[b].astype(np.float64)).transpose(0, 1)
+            kk = torch.from_numpy(K[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+            vv = torch.from_numpy(V[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+            mask = causal_lower_right(lq[b], lk[b]) if causal else None
+            want = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=scale)
+            want = want.transpose(0, 1).numpy()
+            d = np.abs(got[cu_q[b]:cu_q[b + 1]] - want).max()
+            assert d < 1e-12, (b, d)
+
+
+def check_prefix_split(ns):
+    rng = np.random.default_rng(18)
+    L, HQ, HKV, D = 23, 4, 2, 8
+    K, V, Q = _rand(rng, L, HKV, D), _rand(rng, L, HKV, D), _rand(rng, L, HQ, D)
+    full, _ = _prefill_contig(ns, [Q], [K], [V], [L], 0.3, 4, np.random.default_rng(7))
+    for p in (0, 1, 4, 11, 22):
+        part, _ = _prefill_contig(ns, [Q[p:]], [K], [V], [L - p], 0.3, 4, np.random.default_rng(8 + p))
+        assert np.allclose(part, full[p:], atol=1e-14, rtol=0), p
+    dec = _decode_contig(ns, Q[-1:], [K], [V], 0.3, 4, np.random.default_rng(9))
+    assert np.allclose(dec[0], full[-1], atol=1e-14, rtol=0)
+
+
+ALL_CHECKS = [
+    check_slot_teaching, check_slot_boundaries, check_slot_prefill_log, check_slot_decode_log,
+    check_positions, check_store, check_softmax_example, check_hand_example,
+    check_cached_append, check_decode_vs_sdpa, check_block_permutation, check_single_key,
+    check_gqa_is_repeat, check_empty_context, check_partials_merge, check_causal_matrix,
+    check_future_change, check_prefill_vs_sdpa, check_prefix_split,
+]
+
+
+def check_bf16_widening(ns):
+    """bf16 bits widen exactly as torch's own bfloat16 -> float64 conversion."""
+    t = (torch.randn(4096, generator=torch.Generator().manual_seed(3)) * 7).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    got = _oracle.to_f64(bits, "bf16") if ns.to_f64 is None else ns.to_f64(bits, "bf16")
+    assert np.array_equal(got, t.double().numpy())
+
+
+ALL_CHECKS.append(check_bf16_widening)
