@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on MI355X.
+
+A step is one pass of the whole path over one batch of the Qwen3-0.6B-shaped
+decode layer (256 sequences, 16 Q / 8 KV heads, head_dim 128, bf16, block
+size 256, context lengths uniform in [128, 4096]): slot addressing of the new
+tokens, the K/V scatter, the split-K decode pass and the log-sum-exp merge.
+Inputs are resident in HBM before the timed region.  The JSON line reports
+the whole step's algorithmic bytes per second as `value`, the decode pass's
+own HBM roofline, and the CPU oracle timed on a bounded sample of the same
+batch (whose outputs are also compared with the GPU's).  The chunked-prefill
+workload (8 x (1024 cached + 256 new) tokens) is timed as an extra.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(w):
+    """Algorithmic bytes of one decode call: live K/V rows once, q, out, live table entries."""
+    elt = 2 if w.dtype == "bf16" else 4
+    kv = int(w.seq_lens_k.sum()) * w.kv_bytes_per_token
+    q = w.num_seqs * w.num_q_heads * w.head_dim * elt
+    bt = int(np.ceil(w.seq_lens_k / w.block_size).sum()) * 4 + w.num_seqs * 4
+    return kv, q, bt
+
+
+def store_bytes(w):
+    """New K/V rows read and written, plus slot-addressing metadata."""
+    rows = w.num_new_tokens * w.kv_bytes_per_token
+    meta = w.num_seqs * (4 + 4 + 4) + w.num_new_tokens * 4 * 2
+    return 2 * rows + meta
+
+
+def time_decode(args):
+    import torch
+
+    import paged_kv_cache_67_amd as pk
+    from paged_kv_cache_67_amd import harness
+    from workloads import make_config
+
+    log("generating the Qwen3-0.6B decode batch (seed 67002)")
+    w = make_config(2)
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    torch.cuda.synchronize()
+    P = dw.effective_partition
+    max_ctx = w.max_seqlen_k
+    split = dw.workspace is not None
+    log(f"sum(ctx)={int(w.seq_lens_k.sum())} partition={P} split={split}")
+
+    def step(ev=None):
+        dw.slot_mapping()
+        dw.store()
+        if split:
+            if ev is not None:
+                ev[0].record()
+            pk.pa_decode_partitions(dw.q, dw.k_cache, dw.v_cache, dw.block_table, dw.seq_lens_k,
+                                    w.scale, max_ctx, P, dw.workspace)
+            if ev is not None:
+                ev[1].record()
+            pk.pa_decode_merge(dw.out, dw.workspace, dw.seq_lens_k, max_ctx, P)
+        else:
+            if ev is not None:
+                ev[0].record()
+            dw.attention()
+            if ev is not None:
+                ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    log(f"step {ms_step * 1e3:.1f} us; decode pass mean {k_ms.mean() * 1e3:.1f} us "
+        f"(median {np.median(k_ms) * 1e3:.1f})")
+
+    # component times, each in a loop of its own (not part of the reported step time)
+    comp = {}
+    for name, fn in (("slot_mapping", dw.slot_mapping), ("store", dw.store)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(50):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        comp[name + "_us"] = round(a.elapsed_time(b) / 50 * 1e3, 2)
+    if split:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(50):
+            pk.pa_decode_merge(dw.out, dw.workspace, dw.seq_lens_k, max_ctx, P)
+        b.record()
+        torch.cuda.synchronize()
+        comp["merge_us"] = round(a.elapsed_time(b) / 50 * 1e3, 2)
+    step()
+    torch.cuda.synchronize()
+    return w, dw, ms_step, float(k_ms.mean()), comp, P
+
+
+def time_prefill(args):
+    """pa_prefill_paged on the chunked-prefill workload, rotating buffer sets past the MALL."""
+    import torch
+
+    from paged_kv_cache_67_amd import harness
+    from workloads import make_config
+
+    log("prefill: generating 8 x (1024 cached + 256 new) tokens")
+    w = make_config(4)
+    sets = []
+    for _ in range(6):  # 6 x ~90 MB > 256 MB Infinity Cache
+        dw = harness.DeviceWorkload(w, "cuda")
+        dw.load_history()
+        dw.slot_mapping()
+        dw.store()
+        sets.append(dw)
+    torch.cuda.synchronize()
+    for i in range(10):
+        sets[i % len(sets)].attention()
+    n = max(60, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record()
+        sets[i % len(sets)].attention()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    L, lq = int(w.seq_lens_k[0]), int(w.new_lens[0])
+    pairs = sum(L - lq + i + 1 for i in range(lq))  # causal-masked (query, key) pairs per head
+    flops = 4.0 * w.head_dim * pairs * w.num_q_heads * w.num_seqs
+    us = float(np.median(ms)) * 1e3
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"prefill median {us:.1f} us, {tf:.1f} TFLOP/s")
+    return {"workload": w.name, "kernel": "pa_prefill_paged", "us_median": round(us, 2),
+            "us_mean": round(float(ms.mean()) * 1e3, 2), "gflop": round(flops / 1e9, 3),
+            "tflops": round(tf, 1), "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4), "buffer_sets": len(sets)}
+
+
+def cpu_baseline(w, dw, seconds):
+    """Time the CPU oracle on a bounded sample of the same batch; check the GPU on it too."""
+    import oracle
+    from paged_kv_cache_67_amd import harness
+
+    log("cpu baseline: building oracle pools (not timed)")
+    kp, vp = w.empty_pool(), w.empty_pool()
+    oracle.store_kv(kp, vp, w.k_hist, w.v_hist,
+                    oracle.slot_mapping(w.block_table, w.cu_seqlens_hist, w.hist_lens, w.block_size))
+    gpu = oracle.to_f64(harness.from_device(dw.out), w.dtype)
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    done, errs, nbytes = [], [], 0
+    wall0, cpu0 = time.perf_counter(), time.process_time()
+    for b in order:
+        sl = slice(int(b), int(b) + 1)
+        slots = oracle.slot_mapping(w.block_table[sl], np.array([0, 1]), w.seq_lens_k[sl], w.block_size)
+        oracle.store_kv(kp, vp, w.k_new[sl], w.v_new[sl], slots)
+        out = oracle.decode(w.q[sl], kp, vp, w.block_table[sl], w.seq_lens_k[sl], w.scale, w.dtype)
+        done.append(int(b))
+        errs.append(np.abs(out[0] - gpu[b]))
+        kv, q, bt = decode_bytes_sample(w, int(b))
+        nbytes += kv + 2 * q + bt
+        if time.perf_counter() - wall0 >= seconds:
+            break
+    wall = time.perf_counter() - wall0
+    cpu = time.process_time() - cpu0
+    err = np.stack(errs)
+    log(f"cpu baseline: {len(done)} sequences in {wall:.1f} s; parity max {err.max():.2e} mean {err.mean():.2e}")
+    return ({"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+             "kind": "oracle",
+             "sample": f"{len(done)} of {w.num_seqs} sequences (random order, seed 0): slot mapping, "
+                       f"store and fp64 decode, {wall:.1f} s wall"},
+            {"sample_seqs": len(done), "max_err": float(err.max()), "mean_err": float(err.mean()),
+             "ok": bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and np.all(np.isfinite(gpu)))})
+
+
+def decode_bytes_sample(w, b):
+    elt = 2 if w.dtype == "bf16" else 4
+    L = int(w.seq_lens_k[b])
+    return (L * w.kv_bytes_per_token, w.num_q_heads * w.head_dim * elt,
+            int(math.ceil(L / w.block_size)) * 4 + 4)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the paged-attention path needs no collective and this "
+              "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import paged_kv_cache_67_amd as pk
+    pk.lib()  # fails loudly if libpa.so is not built
+
+    w, dw, ms_step, pass_ms, comp, P = time_decode(args)
+    kv, q, bt = decode_bytes(w)
+    pass_bytes = kv + q + bt                       # what the split-K pass must read
+    step_bytes = kv + 2 * q + bt + store_bytes(w)  # + out, + the scatter and its metadata
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = pass_bytes / (pass_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged decode µs/step + achieved HBM GB/s (% of peak), Qwen3-0.6B shape",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size,
+            "context_lens": "uniform [128, 4096], seed 67002",
+            "sum_context_tokens": int(w.seq_lens_k.sum()),
+            "partition_tokens": P,
+            "step": "pa_slot_mapping + pa_store_kv + pa_decode_partitions + pa_decode_merge",
+            "step_bytes": int(step_bytes),
+        },
+        "roofline": {
+            "kernel": "decode split-K pass (pa_decode_partitions)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": int(pass_bytes),
+            "avg_launch_us": round(pass_ms * 1e3, 2),
+        },
+        "components_us": comp,
+    }
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline(w, dw, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+        if not parity["ok"]:
+            result["value"] = None
+            result["note"] = "parity failed on the oracle sample: no time reported"
+    else:
+        result["cpu_baseline"] = None
+    if not args.no_prefill:
+        del dw
+        torch.cuda.empty_cache()
+        result["extra"] = {"prefill": time_prefill(args)}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

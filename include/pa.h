@@ -1,0 +1,262 @@
+/*
+ * pa.h -- paged attention over a block-managed KV cache, for AMD Instinct
+ * MI355X (gfx950).  C ABI; every function is extern "C".
+ *
+ * Sources cited below:
+ *   [Lab]      "5. 动手改造：从跑通到可测量的推理服务", the nano-vLLM inference
+ *              lab manual (duanmeng.github.io, 实验手册.html), appendix B.
+ *   [mini]     "mini-vLLM v0.4 -- From-Scratch LLM Inference Serving Runtime"
+ *              (shadowgraph.io/WJX3078/mini-vllm), section 5.
+ *   [MinivLLM] "MinivLLM：六步搭出一个 Qwen3 推理引擎，再核清四处文档与代码的分岔"
+ *              (txtmix.com), section "注意力内核的三个分支".
+ *   [KVblog]   "大模型推理引擎学习入门-2：带你理解 nano-vllm 的 KV Cache 以及
+ *              Paged Attention" (juejin.cn), sections 3.1, 3.5 and 4.4.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named *cache*, q, out, key, value, workspace, block_table,
+ *   slot_mapping, context_lens, seq_lens_k and cu_seqlens_* are DEVICE
+ *   pointers owned by the caller.  The library allocates no device memory,
+ *   keeps no pointer after a call returns and has no mutable global state
+ *   except a thread-local error message.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream): it validates its host-side arguments, enqueues its kernels and
+ *   returns.  It performs no host<->device copies and no synchronisation.
+ *   Inputs must stay alive and unchanged until the stream reaches the work.
+ * - KV pool layout ([KVblog] 3.1: kv_cache is (2, layers, num_blocks,
+ *   block_size, kv_heads, head_dim); one layer's K or V pool):
+ *       cache[num_blocks][block_size][num_kv_heads][head_dim], contiguous.
+ *   Logical token t of a sequence lives in block block_table[t / block_size]
+ *   at row t % block_size ([MinivLLM], paged_attention_decode_kernel).
+ * - block_table is int32 [num_seqs][max_blocks_per_seq], row-major, padded
+ *   with -1 past each sequence's last block ([MinivLLM], prepare_decode).
+ * - Element types: PA_F32 (float) or PA_BF16 (bfloat16 bits); q, out, key,
+ *   value and both caches share one type.  head_dim is 64 or 128.
+ *   block_size is a power of two in [8, 1024].
+ * - Base pointers of q, out, key, value, caches and workspace must be 16-byte
+ *   aligned.
+ * - Arithmetic: fp32 accumulation; bf16 results are rounded to nearest-even.
+ * - Device-side contents (slot values, block ids, lengths) are the caller's
+ *   contract and are not validated on the host: slot_mapping entries are -1
+ *   or in [0, num_blocks*block_size) and distinct; block ids read for live
+ *   tokens are in [0, num_blocks); 0 <= context_lens[b] <= max_context_len.
+ *   The kernels never read or write outside the buffers their sizes describe
+ *   even when the contract is broken: an out-of-range slot is skipped, and a
+ *   live token whose block id is out of range turns that sequence's output
+ *   into NaN instead of being read.
+ * - Return value: a pa_status.  On failure nothing has been enqueued and
+ *   pa_last_error() describes the problem.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is negative or sizes are inconsistent */
+  PA_ERR_UNSUPPORTED = 3, /* dtype / head_dim / block_size / head ratio without a kernel */
+  PA_ERR_ALIGN = 4,       /* a pointer or stride breaks the 16-byte alignment rule */
+  PA_ERR_WORKSPACE = 5,   /* workspace smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_slot_mapping -- physical cache row of every new token.
+ *
+ * [KVblog] 3.1 and 3.5, [Lab] B.2.3: the token at logical position p of a
+ * sequence is written to row slot = block_table[p / block_size] * block_size
+ * + p % block_size of the flattened pool.  Sequence b contributes the new
+ * tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1; they are its last
+ * Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] tokens out of seq_lens_k[b], so
+ * new token i sits at p = seq_lens_k[b] - Lq + i (a cached prefix shifts
+ * positions, [KVblog] 3.5; a decode step has Lq = 1 and p = context_len - 1,
+ * [KVblog] 4.4).
+ *
+ *   slot_mapping  out  int32 [num_tokens]
+ *   block_table   in   int32 [num_seqs][max_blocks_per_seq]
+ *   cu_seqlens_q  in   int32 [num_seqs + 1], non-decreasing, cu[0] = 0,
+ *                      cu[num_seqs] = num_tokens
+ *   seq_lens_k    in   int32 [num_seqs], seq_lens_k[b] >= Lq of b
+ *
+ * A token whose logical block index is >= max_blocks_per_seq, or whose table
+ * entry is outside [0, num_blocks), gets slot -1 (the pages' "do not write"
+ * marker).  num_seqs = 0 or num_tokens = 0 is a no-op.
+ */
+int pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_table,
+                    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                    const int32_t* seq_lens_k, int32_t num_seqs, int32_t num_tokens,
+                    int32_t block_size, int32_t num_blocks, void* stream);
+
+/*
+ * pa_store_kv -- scatter this step's K and V rows into the paged pool.
+ *
+ * [MinivLLM] store_kvcache_kernel and [KVblog] 3.1 (the physical layer):
+ * for every token t with s = slot_mapping[t] != -1,
+ *   k_cache[s / block_size][s % block_size][:][:] = key[t][:][:]
+ *   v_cache[s / block_size][s % block_size][:][:] = value[t][:][:]
+ * A bitwise copy.  Slots outside [0, num_blocks*block_size) are skipped like
+ * -1.  Two tokens must not share a slot.
+ *
+ *   key, value   in   [num_tokens][num_kv_heads][head_dim]; the [kv_heads,
+ *                     head_dim] row of a token is contiguous and consecutive
+ *                     tokens are key_token_stride / value_token_stride
+ *                     ELEMENTS apart (so views into a fused qkv tensor work);
+ *                     the strides times the element size must be multiples
+ *                     of 16 bytes
+ *   k_cache, v_cache  in/out pools, layout above
+ *   slot_mapping in   int32 [num_tokens]
+ */
+int pa_store_kv(const void* key, const void* value, int64_t key_token_stride,
+                int64_t value_token_stride, void* k_cache, void* v_cache,
+                const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                void* stream);
+
+/*
+ * Split-K (flash-decoding) partitioning of decode.
+ *
+ * pa_decode splits each sequence's keys into partitions of partition_size
+ * tokens; partition p covers keys [p*P, min((p+1)*P, L)).  Each partition
+ * produces the online-softmax state of [mini] section 5 ((m, l, acc): running
+ * max, exp-sum and weighted V sum) and a second kernel merges the states with
+ * the rescaling of [Lab] Fig. B-5 (pa_decode_merge).
+ *
+ * pa_decode_partition_size returns the partition size pa_decode uses when
+ * asked for the automatic choice (partition_size = 0): a power of two of at
+ * least 256 that gives the launch enough workgroups for 256 compute units,
+ * or max_context_len rounded up (one partition, no merge) when one pass
+ * already fills the chip.  Returns a negative pa_status on bad arguments.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t block_size);
+
+/*
+ * Bytes of workspace pa_decode needs for `partition_size` (> 0): 0 when one
+ * partition covers max_context_len.  Layout, with NP =
+ * ceil(max_context_len / partition_size), all float32, back to back:
+ *   acc [num_seqs][num_q_heads][NP][head_dim]   sum_j exp(s_j - m) v_j
+ *   m   [num_seqs][num_q_heads][NP]             max_j s_j (natural-log units,
+ *                                               s_j = scale * q . k_j)
+ *   l   [num_seqs][num_q_heads][NP]             sum_j exp(s_j - m)
+ * Only partitions with p*P < context_lens[b] are written.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode -- decode attention (one query token per sequence) over the pool.
+ *
+ * [mini] section 5 and [MinivLLM] paged_attention_decode_kernel: for sequence
+ * b with L = context_lens[b] keys (L counts the token stored this step,
+ * [KVblog] 4.4) and query head h served by KV head g = h / (num_q_heads /
+ * num_kv_heads) (GQA, [mini] 5):
+ *   out[b][h] = softmax_j(scale * q[b][h] . K_g[j]) . V_g[j],  j < L,
+ * with K/V rows read through block_table and never copied to a contiguous
+ * buffer.  `scale` is the final multiplier of q.k (no internal 1/sqrt(D)).
+ * L = 0 gives an all-zero output row.
+ *
+ *   out          out  [num_seqs][num_q_heads][head_dim]
+ *   q            in   [num_seqs][num_q_heads][head_dim]
+ *   context_lens in   int32 [num_seqs]
+ *   max_context_len   host upper bound of context_lens (sizes the grid);
+ *                     <= 0 means max_blocks_per_seq * block_size
+ *   partition_size    0 = automatic (pa_decode_partition_size); -1 = one
+ *                     partition per sequence (single pass, no workspace);
+ *                     otherwise a power of two >= 16
+ *   workspace         device scratch of workspace_bytes bytes; required when
+ *                     the partitioning has more than one partition.  With the
+ *                     automatic choice and workspace == NULL the call runs a
+ *                     single pass instead.  After the call it holds the
+ *                     partition states in the layout given above.
+ * num_q_heads must be a multiple of num_kv_heads.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_table, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+              int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, float scale, pa_dtype dtype,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_partitions -- the first pass of split-K decode on its own.
+ *
+ * Same arguments and meaning as pa_decode, without `out`: it computes, for
+ * every (sequence, query head, partition) with p*P < context_lens[b], the
+ * online-softmax state of [mini] section 5 over keys [p*P, min((p+1)*P, L))
+ * and writes it to `workspace` in the layout above.  partition_size must be
+ * a power of two >= 16 and < max_context_len (an actual split).
+ * pa_decode = pa_decode_partitions + pa_decode_merge.
+ */
+int pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                         int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, float scale, pa_dtype dtype,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * pa_decode_merge -- the second pass of split-K decode on its own.
+ *
+ * Reads partition states in the workspace layout above and writes
+ *   out[b][h] = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p,  M = max_p m_p
+ * over the ceil(context_lens[b] / partition_size) partitions of b ([Lab]
+ * Fig. B-5 rescaling; zero partitions give 0).  pa_decode calls the same
+ * kernel; it is exported so the merge can be driven with states produced
+ * elsewhere (e.g. partitions of one sequence computed on several devices).
+ */
+int pa_decode_merge(void* out, const void* workspace, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_context_len, int32_t partition_size, pa_dtype dtype,
+                    void* stream);
+
+/*
+ * pa_prefill_paged -- varlen (chunked) prefill attention over a cached prefix.
+ *
+ * [KVblog] 3.5: sequence b has Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] new
+ * query tokens and Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys; the first
+ * Lk - Lq keys are the cached prefix and every key is read from the pool
+ * through block_table (the new chunk's rows must have been stored first,
+ * [MinivLLM]: Attention.forward writes the cache, then attends).  Query i of
+ * b sits at position Lk - Lq + i ([Lab] B.6) and, with causal != 0, sees keys
+ * j <= Lk - Lq + i; with causal == 0 it sees all Lk keys.
+ *
+ *   out          out  [total_q][num_q_heads][head_dim]
+ *   q            in   [total_q][num_q_heads][head_dim]
+ *   cu_seqlens_q in   int32 [num_seqs + 1], cu[num_seqs] = total_q
+ *   cu_seqlens_k in   int32 [num_seqs + 1], Lk >= Lq for every sequence
+ *   max_seqlen_q / max_seqlen_k   host upper bounds of Lq / Lk
+ *
+ * dtype must be PA_BF16 (the matrix-core path).
+ */
+int pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                     int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                     int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
+                     pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

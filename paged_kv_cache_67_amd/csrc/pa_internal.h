@@ -1,0 +1,71 @@
+// Internal helpers shared by the libpa kernels and entry points (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// Host side: error reporting.  Each entry point returns a pa_status and leaves
+// a human-readable detail in a thread-local buffer.
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+// Check the launch that was just enqueued; returns PA_OK or PA_ERR_HIP.
+int check_launch(const char* what);
+
+inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int elt_bytes(pa_dtype t) { return t == PA_BF16 ? 2 : 4; }
+
+constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
+
+// ---------------------------------------------------------------------------
+// Device side.
+
+// bf16 <-> fp32.  A bf16 value is the top half of an fp32, so widening is a
+// shift; narrowing rounds to nearest-even (NaN stays NaN).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// DPP lane moves within a 16-lane row (all source lanes valid for these
+// patterns, so bound_ctrl does not matter).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane of the
+// group receives the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppRowHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
+  if constexpr (N == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace pa

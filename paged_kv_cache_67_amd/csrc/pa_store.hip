@@ -1,0 +1,121 @@
+// a1 slot addressing and a2 K/V scatter into the paged pool (gfx950).
+//
+// Slot addressing follows "大模型推理引擎学习入门-2 ... nano-vllm 的 KV Cache 以及
+// Paged Attention" (juejin.cn) section 3.5: slot = block_table[p / B] * B + p % B.
+// The scatter follows the store_kvcache kernel described in "MinivLLM：六步搭出
+// 一个 Qwen3 推理引擎" (txtmix.com), section "注意力内核的三个分支": one row per
+// token, slot -1 means "do not write".
+#include <limits.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+// One workgroup per sequence; its threads stride over the sequence's new tokens.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    int32_t* __restrict__ slots, const int32_t* __restrict__ block_table, int maxb,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ lens_k, int num_tokens,
+    int bs_log2, int num_blocks) {
+  const int b = blockIdx.x;
+  const int q0 = cu_q[b];
+  const int lq = cu_q[b + 1] - q0;
+  const int lk = lens_k[b];
+  const int bs = 1 << bs_log2;
+  const int32_t* row = block_table + (int64_t)b * maxb;
+  for (int i = threadIdx.x; i < lq; i += blockDim.x) {
+    const int t = q0 + i;
+    if (t < 0 || t >= num_tokens) continue;
+    const int p = lk - lq + i;
+    int s = -1;
+    if (p >= 0 && (p >> bs_log2) < maxb) {
+      const int blk = row[p >> bs_log2];
+      if (blk >= 0 && blk < num_blocks) s = blk * bs + (p & (bs - 1));
+    }
+    slots[t] = s;
+  }
+}
+
+// Flat 16-byte copy: work item = (token, 16-byte chunk of its [kv_heads, head_dim] row).
+__global__ __launch_bounds__(256) void store_kv_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, int64_t key_stride_bytes,
+    int64_t value_stride_bytes, char* __restrict__ kc, char* __restrict__ vc,
+    const int32_t* __restrict__ slots, int64_t num_items, int row_chunks, int64_t num_slots,
+    int64_t row_bytes) {
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < num_items; i += step) {
+    const int64_t t = i / row_chunks;
+    const int c = int(i - t * row_chunks);
+    const int s = slots[t];
+    if (s < 0 || s >= num_slots) continue;
+    const uint4 k = reinterpret_cast<const uint4*>(key + t * key_stride_bytes)[c];
+    const uint4 v = reinterpret_cast<const uint4*>(value + t * value_stride_bytes)[c];
+    reinterpret_cast<uint4*>(kc + (int64_t)s * row_bytes)[c] = k;
+    reinterpret_cast<uint4*>(vc + (int64_t)s * row_bytes)[c] = v;
+  }
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                               const int32_t* seq_lens_k, int32_t num_seqs, int32_t num_tokens,
+                               int32_t block_size, int32_t num_blocks, void* stream) {
+  clear_error();
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "pa_slot_mapping: negative size");
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "pa_slot_mapping: block_size %d not a power of two in [8,1024]",
+                block_size);
+  if ((int64_t)num_blocks * block_size > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_slot_mapping: num_blocks*block_size exceeds int32 slots");
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (max_blocks_per_seq == 0) return fail(PA_ERR_SHAPE, "pa_slot_mapping: max_blocks_per_seq is 0");
+  if (!slot_mapping || !block_table || !cu_seqlens_q || !seq_lens_k)
+    return fail(PA_ERR_NULL, "pa_slot_mapping: null pointer");
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, (hipStream_t)stream,
+                     slot_mapping, block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens_k,
+                     num_tokens, __builtin_ctz(block_size), num_blocks);
+  return check_launch("pa_slot_mapping");
+}
+
+extern "C" int pa_store_kv(const void* key, const void* value, int64_t key_token_stride,
+                           int64_t value_token_stride, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           pa_dtype dtype, void* stream) {
+  clear_error();
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PA_ERR_SHAPE, "pa_store_kv: bad size (tokens %d, blocks %d, kv_heads %d, dim %d)",
+                num_tokens, num_blocks, num_kv_heads, head_dim);
+  if (dtype != PA_F32 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_store_kv: dtype %d", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_store_kv: head_dim %d (64 or 128)", head_dim);
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "pa_store_kv: block_size %d not a power of two in [8,1024]",
+                block_size);
+  if ((int64_t)num_blocks * block_size > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_store_kv: num_blocks*block_size exceeds int32 slots");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_NULL, "pa_store_kv: null pointer");
+  const int eb = elt_bytes(dtype);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * eb;
+  if (key_token_stride < (int64_t)num_kv_heads * head_dim ||
+      value_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "pa_store_kv: token stride smaller than a row");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
+    return fail(PA_ERR_ALIGN, "pa_store_kv: pointers and token strides must be 16-byte aligned");
+  const int row_chunks = int(row_bytes / 16);
+  const int64_t items = (int64_t)num_tokens * row_chunks;
+  const int64_t blocks = (items + 255) / 256;
+  const int grid = int(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(store_kv_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     (const char*)key, (const char*)value, key_token_stride * eb,
+                     value_token_stride * eb, (char*)k_cache, (char*)v_cache, slot_mapping, items,
+                     row_chunks, (int64_t)num_blocks * block_size, row_bytes);
+  return check_launch("pa_store_kv");
+}
