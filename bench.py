@@ -62,10 +62,10 @@ def time_decode(args):
 
     log("generating the Qwen3-0.6B decode batch (seed 67002)")
     w = make_config(2)
-    dw = harness.DeviceWorkload(w, "cuda")
+    dw = harness.DeviceWorkload(w, "cuda", partition_size=args.partition)
     dw.load_history()
     torch.cuda.synchronize()
-    P = dw.effective_partition
+    P = args.partition
     max_ctx = w.max_seqlen_k
     split = dw.workspace is not None
     log(f"sum(ctx)={int(w.seq_lens_k.sum())} partition={P} split={split}")
@@ -73,17 +73,15 @@ def time_decode(args):
     def step(ev=None):
         dw.slot_mapping()
         dw.store()
+        if ev is not None:
+            ev[0].record()
         if split:
-            if ev is not None:
-                ev[0].record()
-            pk.pa_decode_partitions(dw.q, dw.k_cache, dw.v_cache, dw.block_table, dw.seq_lens_k,
-                                    w.scale, max_ctx, P, dw.workspace)
+            pk.pa_decode_partitions(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_table,
+                                    dw.seq_lens_k, w.scale, max_ctx, P, dw.workspace)
             if ev is not None:
                 ev[1].record()
-            pk.pa_decode_merge(dw.out, dw.workspace, dw.seq_lens_k, max_ctx, P)
+            pk.pa_decode_merge(dw.out, dw.workspace, dw.seq_lens_k, w.num_kv_heads, max_ctx, P)
         else:
-            if ev is not None:
-                ev[0].record()
             dw.attention()
             if ev is not None:
                 ev[1].record()
@@ -120,7 +118,7 @@ def time_decode(args):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(50):
-            pk.pa_decode_merge(dw.out, dw.workspace, dw.seq_lens_k, max_ctx, P)
+            pk.pa_decode_merge(dw.out, dw.workspace, dw.seq_lens_k, w.num_kv_heads, max_ctx, P)
         b.record()
         torch.cuda.synchronize()
         comp["merge_us"] = round(a.elapsed_time(b) / 50 * 1e3, 2)
@@ -220,6 +218,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="decode split: 0 balanced (default), -1 single pass, P fixed partitions")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the paged-attention path needs no collective and this "
@@ -261,12 +261,12 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size,
             "context_lens": "uniform [128, 4096], seed 67002",
             "sum_context_tokens": int(w.seq_lens_k.sum()),
-            "partition_tokens": P,
+            "split": {0: "balanced split-K", -1: "single pass"}.get(P, f"fixed {P}-token partitions"),
             "step": "pa_slot_mapping + pa_store_kv + pa_decode_partitions + pa_decode_merge",
             "step_bytes": int(step_bytes),
         },
         "roofline": {
-            "kernel": "decode split-K pass (pa_decode_partitions)",
+            "kernel": "decode first pass (pa_decode_partitions)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -131,35 +131,44 @@ int pa_store_kv(const void* key, const void* value, int64_t key_token_stride,
                 void* stream);
 
 /*
- * Split-K (flash-decoding) partitioning of decode.
+ * Split-K (flash-decoding) for decode.
  *
- * pa_decode splits each sequence's keys into partitions of partition_size
- * tokens; partition p covers keys [p*P, min((p+1)*P, L)).  Each partition
- * produces the online-softmax state of [mini] section 5 ((m, l, acc): running
- * max, exp-sum and weighted V sum) and a second kernel merges the states with
- * the rescaling of [Lab] Fig. B-5 (pa_decode_merge).
+ * A long context is split into pieces; each piece produces the online-softmax
+ * state of [mini] section 5 -- (m, l, acc): max score, exp-sum and weighted V
+ * sum over its keys -- and a second kernel (pa_decode_merge) combines the
+ * pieces of a sequence with the rescaling of [Lab] Fig. B-5:
+ *   out = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p,  M = max_p m_p.
+ * partition_size selects how keys are split:
+ *    0  balanced (default): every sequence's keys, in chunks of 8-32 tokens,
+ *       are laid end to end and each KV head's keys are cut into equal slices,
+ *       one per wave, whatever the sequence boundaries; a sequence inside one
+ *       slice is finished in the first pass.  Balances mixed lengths.
+ *       Needs num_seqs <= 8192; larger batches fall back to fixed partitions
+ *       with an automatic size.  Without a workspace: single pass.
+ *   -1  single pass: one piece per sequence, no workspace, no merge.
+ *  P>0  fixed partitions: a power of two >= 16; partition p of sequence b
+ *       covers keys [p*P, min((p+1)*P, L)).
  *
- * pa_decode_partition_size returns the partition size pa_decode uses when
- * asked for the automatic choice (partition_size = 0): a power of two of at
- * least 256 that gives the launch enough workgroups for 256 compute units,
- * or max_context_len rounded up (one partition, no merge) when one pass
- * already fills the chip.  Returns a negative pa_status on bad arguments.
+ * Workspace layouts (float32 unless noted, back to back):
+ *  fixed, NP = ceil(max_context_len / P), written for partitions with p*P < L:
+ *    acc [num_seqs][num_q_heads][NP][head_dim]   sum_j exp(s_j - m) v_j
+ *    m   [num_seqs][num_q_heads][NP]             max_j s_j, s_j = scale q.k_j
+ *    l   [num_seqs][num_q_heads][NP]             sum_j exp(s_j - m)
+ *  balanced, W slices per KV-head wave (chosen by the library):
+ *    acc [num_q_heads][W][2][head_dim], m [num_q_heads][W][2],
+ *    l [num_q_heads][W][2], then int32 [num_seqs + 1] prefix sums of the
+ *    per-sequence chunk counts; slot 0 of slice w holds the piece whose
+ *    sequence began before the slice, slot 1 the piece that runs past it.
  */
-int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                 int32_t max_context_len, int32_t block_size);
 
 /*
- * Bytes of workspace pa_decode needs for `partition_size` (> 0): 0 when one
- * partition covers max_context_len.  Layout, with NP =
- * ceil(max_context_len / partition_size), all float32, back to back:
- *   acc [num_seqs][num_q_heads][NP][head_dim]   sum_j exp(s_j - m) v_j
- *   m   [num_seqs][num_q_heads][NP]             max_j s_j (natural-log units,
- *                                               s_j = scale * q . k_j)
- *   l   [num_seqs][num_q_heads][NP]             sum_j exp(s_j - m)
- * Only partitions with p*P < context_lens[b] are written.
+ * Bytes of workspace pa_decode needs for `partition_size` (0, -1 or P), for
+ * either element type: 0 when the call runs a single pass.  Returns 0 for
+ * invalid sizes.
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_size);
 
 /*
  * pa_decode -- decode attention (one query token per sequence) over the pool.
@@ -176,16 +185,11 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   out          out  [num_seqs][num_q_heads][head_dim]
  *   q            in   [num_seqs][num_q_heads][head_dim]
  *   context_lens in   int32 [num_seqs]
- *   max_context_len   host upper bound of context_lens (sizes the grid);
+ *   max_context_len   host upper bound of context_lens (sizes the split);
  *                     <= 0 means max_blocks_per_seq * block_size
- *   partition_size    0 = automatic (pa_decode_partition_size); -1 = one
- *                     partition per sequence (single pass, no workspace);
- *                     otherwise a power of two >= 16
- *   workspace         device scratch of workspace_bytes bytes; required when
- *                     the partitioning has more than one partition.  With the
- *                     automatic choice and workspace == NULL the call runs a
- *                     single pass instead.  After the call it holds the
- *                     partition states in the layout given above.
+ *   partition_size    0 / -1 / P, see "Split-K" above
+ *   workspace         device scratch of workspace_bytes bytes (see
+ *                     pa_decode_workspace_size); required by a split.
  * num_q_heads must be a multiple of num_kv_heads.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -196,16 +200,17 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * pa_decode_partitions -- the first pass of split-K decode on its own.
+ * pa_decode_partitions -- the first pass of a split decode on its own.
  *
- * Same arguments and meaning as pa_decode, without `out`: it computes, for
- * every (sequence, query head, partition) with p*P < context_lens[b], the
- * online-softmax state of [mini] section 5 over keys [p*P, min((p+1)*P, L))
- * and writes it to `workspace` in the layout above.  partition_size must be
- * a power of two >= 16 and < max_context_len (an actual split).
+ * Same arguments and meaning as pa_decode; partition_size must be 0 or a P
+ * that splits max_context_len, and a workspace is required.  It writes every
+ * piece's online-softmax state ([mini] section 5) to the workspace in the
+ * layout above; with the balanced split it also writes the final rows of the
+ * sequences that no slice boundary cuts to `out` (fixed partitions do not
+ * touch `out`, which may then be NULL).
  * pa_decode = pa_decode_partitions + pa_decode_merge.
  */
-int pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                          int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
@@ -214,19 +219,18 @@ int pa_decode_partitions(const void* q, const void* k_cache, const void* v_cache
                          void* stream);
 
 /*
- * pa_decode_merge -- the second pass of split-K decode on its own.
+ * pa_decode_merge -- the second pass of a split decode on its own.
  *
- * Reads partition states in the workspace layout above and writes
- *   out[b][h] = sum_p e^(m_p - M) acc_p / sum_p e^(m_p - M) l_p,  M = max_p m_p
- * over the ceil(context_lens[b] / partition_size) partitions of b ([Lab]
- * Fig. B-5 rescaling; zero partitions give 0).  pa_decode calls the same
- * kernel; it is exported so the merge can be driven with states produced
- * elsewhere (e.g. partitions of one sequence computed on several devices).
+ * Reads piece states in the workspace layout of `partition_size` (0 or P)
+ * and writes the rows the first pass left open ([Lab] Fig. B-5 rescaling;
+ * a sequence without keys gives a zero row).  Exported so a merge can be
+ * driven with states produced elsewhere, e.g. fixed partitions of one
+ * sequence computed on several devices.
  */
 int pa_decode_merge(void* out, const void* workspace, const int32_t* context_lens,
-                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                    int32_t max_context_len, int32_t partition_size, pa_dtype dtype,
-                    void* stream);
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                    pa_dtype dtype, void* stream);
 
 /*
  * pa_prefill_paged -- varlen (chunked) prefill attention over a cached prefix.

@@ -15,7 +15,6 @@ from ._binding import (  # noqa: F401
     lib_path,
     pa_decode,
     pa_decode_merge,
-    pa_decode_partition_size,
     pa_decode_partitions,
     pa_decode_workspace_size,
     pa_last_error,

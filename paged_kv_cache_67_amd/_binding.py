@@ -30,13 +30,12 @@ SIGNATURES = {
     "pa_slot_mapping": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_store_kv": (C.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                               C.c_int, _vp]),
-    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
-    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                             _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
-    "pa_decode_partitions": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
-                                       _i32, _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
-    "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_decode_partitions": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
+    "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pa_prefill_paged": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                    _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int, _vp]),
 }
@@ -134,16 +133,10 @@ def pa_store_kv(key, value, k_cache, v_cache, slot_mapping, stream=None):
         _ptr(slot_mapping), N, NB, BS, HKV, D, _dtype(k_cache), _stream(stream)))
 
 
-def pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, block_size) -> int:
-    p = lib().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, block_size)
-    if p < 0:
-        raise PAError("pa_decode_partition_size", -p, pa_last_error())
-    return p
-
-
-def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size) -> int:
-    return lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
-                                          partition_size)
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                             partition_size=0) -> int:
+    return lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          max_context_len, partition_size)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_table, context_lens, scale, max_context_len=0,
@@ -162,27 +155,30 @@ def pa_decode(out, q, k_cache, v_cache, block_table, context_lens, scale, max_co
         _dtype(q), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def pa_decode_partitions(q, k_cache, v_cache, block_table, context_lens, scale, max_context_len,
+def pa_decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, scale, max_context_len,
                          partition_size, workspace, stream=None):
     B, HQ, D = q.shape
     NB, BS, HKV, Dk = k_cache.shape
     assert Dk == D and v_cache.shape == k_cache.shape and q.dtype == k_cache.dtype
     assert q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
     assert block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.shape[0] == B
+    if out is not None:
+        assert out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
     _i32_vec(context_lens, B, "context_lens")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("pa_decode_partitions", lib().pa_decode_partitions(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(context_lens), B, int(max_context_len), NB, BS, HQ, HKV, D, float(scale), _dtype(q),
         int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def pa_decode_merge(out, workspace, context_lens, max_context_len, partition_size, stream=None):
+def pa_decode_merge(out, workspace, context_lens, num_kv_heads, max_context_len, partition_size,
+                    stream=None):
     B, HQ, D = out.shape
     _i32_vec(context_lens, B, "context_lens")
     _check("pa_decode_merge", lib().pa_decode_merge(
-        _ptr(out), _ptr(workspace), _ptr(context_lens), B, HQ, D, int(max_context_len),
-        int(partition_size), _dtype(out), _stream(stream)))
+        _ptr(out), _ptr(workspace), _ptr(context_lens), B, HQ, int(num_kv_heads), D,
+        int(max_context_len), int(partition_size), _dtype(out), _stream(stream)))
 
 
 def pa_prefill_paged(out, q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seqlens_k,

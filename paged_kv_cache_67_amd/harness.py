@@ -61,16 +61,12 @@ class DeviceWorkload:
         self.max_context_len = w.max_seqlen_k
         self.partition_size = partition_size
         self.workspace = None
-        if w.kind == "decode":
-            P = partition_size
-            if P == 0:
-                P = pa.pa_decode_partition_size(w.num_seqs, w.num_kv_heads, max(1, self.max_context_len),
-                                                w.block_size)
-            self.effective_partition = P
-            nbytes = (pa.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.head_dim,
-                                                  max(1, self.max_context_len), P) if P > 0 else 0)
-            if with_workspace and nbytes:
-                self.workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        if w.kind == "decode" and with_workspace:
+            nbytes = pa.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                 w.head_dim, max(1, self.max_context_len),
+                                                 partition_size)
+            if nbytes:
+                self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=dev)
 
     # -- the cached history (not part of a step) ------------------------------------
     def load_history(self, stream=None):

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for must in ("pa_slot_mapping", "pa_store_kv", "pa_decode", "pa_decode_merge",
-                 "pa_prefill_paged", "pa_decode_workspace_size", "pa_decode_partition_size", "pa_decode_partitions",
+                 "pa_prefill_paged", "pa_decode_workspace_size", "pa_decode_partitions",
                  "pa_status_string", "pa_last_error", "pa_version"):
         assert must in names
 
@@ -93,22 +93,26 @@ def test_alignment_and_workspace_errors(L):
     assert L.pa_decode(a, a, a, mis, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, None, 0, None) == 4
     # explicit split without enough workspace
     assert L.pa_decode(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 16, None, 0, None) == 5
-    need = L.pa_decode_workspace_size(2, 4, 64, 64, 16)
+    need = L.pa_decode_workspace_size(2, 4, 2, 64, 64, 16)
     assert L.pa_decode(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 16, a, need - 4, None) == 5
+    need0 = L.pa_decode_workspace_size(2, 4, 2, 64, 64, 0)
+    assert L.pa_decode(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, a, 16, None) == 5
     assert L.pa_decode(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 24, a, need, None) == 3
+    # the first pass alone needs a split and a workspace
+    assert L.pa_decode_partitions(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, -1, a, need, None) == 5
+    assert L.pa_decode_partitions(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 128, a, need, None) == 3
+    assert L.pa_decode_partitions(None, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, a, need0, None) == 1
 
 
 def test_workspace_size_closed_form(L):
-    # [B][HQ][NP][D] acc + [B][HQ][NP] m + l, float32
-    assert L.pa_decode_workspace_size(256, 16, 128, 4096, 512) == 256 * 16 * 8 * 130 * 4
-    assert L.pa_decode_workspace_size(8, 16, 128, 32768, 256) == 8 * 16 * 128 * 130 * 4
-    assert L.pa_decode_workspace_size(2, 2, 64, 33, 256) == 0  # one partition: no workspace
-    assert L.pa_decode_workspace_size(2, 2, 64, 33, 16) == 2 * 2 * 3 * 66 * 4
-
-
-def test_auto_partition(L):
-    assert pk.pa_decode_partition_size(256, 8, 4096, 256) == 512   # Qwen3-0.6B decode batch
-    assert pk.pa_decode_partition_size(8, 8, 32768, 256) == 256    # skewed long context
-    assert pk.pa_decode_partition_size(64, 2, 2048, 16) == 256     # Qwen2.5-0.5B decode batch
-    assert pk.pa_decode_partition_size(2, 1, 33, 16) >= 33         # tiny: one pass
-    assert pk.pa_decode_partition_size(4096, 8, 512, 256) >= 512   # big batch, short ctx: one pass
+    # fixed partitions: [B][HQ][NP][D] acc + [B][HQ][NP] m + l, float32
+    assert L.pa_decode_workspace_size(256, 16, 8, 128, 4096, 512) == 256 * 16 * 8 * 130 * 4
+    assert L.pa_decode_workspace_size(8, 16, 8, 128, 32768, 256) == 8 * 16 * 128 * 130 * 4
+    assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 256) == 0   # one partition: no workspace
+    assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 16) == 2 * 2 * 3 * 66 * 4
+    assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, -1) == 0    # single pass
+    # balanced: [HQ][W][2] states + (B+1) int32; W = 2048 waves / 8 KV-head waves
+    assert L.pa_decode_workspace_size(256, 16, 8, 128, 4096, 0) == 16 * 256 * 2 * 130 * 4 + 257 * 4
+    # W is capped by the number of chunks there can be (fp32 d64 chunk: 16 tokens)
+    assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 0) == 2 * 6 * 2 * 66 * 4 + 3 * 4
+    assert L.pa_decode_workspace_size(2, 3, 2, 64, 33, 0) == 0     # invalid head ratio

@@ -94,8 +94,7 @@ def test_decode_matches_oracle(idx):
 def test_decode_qwen3_full_size_sampled():
     """The benchmarked configuration (B=256, auto split-K) on a sample of sequences."""
     w = config(2)
-    P = pk.pa_decode_partition_size(w.num_seqs, w.num_kv_heads, w.max_seqlen_k, w.block_size)
-    announce(f"decode cfg2 full size, partition {P}")
+    announce("decode cfg2 full size, balanced split")
     dw = run_hip(w)
     got = out_f64(dw.out, w.dtype)
     rng = np.random.default_rng(2)
@@ -158,7 +157,7 @@ def test_merge_of_oracle_states():
     announce("merge of oracle partition states")
     out = torch.empty(B, HQ, D, dtype=torch.bfloat16, device="cuda")
     pk.pa_decode_merge(out, torch.from_numpy(ws).cuda(),
-                       torch.from_numpy(w.seq_lens_k).cuda(), w.max_seqlen_k, P)
+                       torch.from_numpy(w.seq_lens_k).cuda(), w.num_kv_heads, w.max_seqlen_k, P)
     torch.cuda.synchronize()
     assert_close(out_f64(out, "bf16"), want, "bf16", "merge")
 
@@ -207,7 +206,8 @@ def test_decode_zero_context_rows():
     dw.load_history()
     dw.step()
     ctx = torch.tensor([5, 0, 0], dtype=torch.int32, device="cuda")
-    nbytes = pk.pa_decode_workspace_size(3, 4, 64, 20, 16)
+    nbytes = max(pk.pa_decode_workspace_size(3, 4, 2, 64, 20, 16),
+                 pk.pa_decode_workspace_size(3, 4, 2, 64, 20, 0))
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     for P in (0, 16, -1):
         out = torch.full_like(dw.out, float("nan"))
@@ -228,9 +228,10 @@ def test_decode_block_permutation_bitwise():
     rng = np.random.default_rng(99)
     perm = rng.permutation(b.num_blocks).astype(np.int32)
     b.block_table = np.where(b.block_table >= 0, perm[np.maximum(b.block_table, 0)], -1).astype(np.int32)
-    announce("decode block permutation")
-    oa, ob = run_hip(a, partition_size=64), run_hip(b, partition_size=64)
-    assert bits_equal(harness.from_device(oa.out), harness.from_device(ob.out))
+    for P in (64, 0):
+        announce(f"decode block permutation, partition {P}")
+        oa, ob = run_hip(a, partition_size=P), run_hip(b, partition_size=P)
+        assert bits_equal(harness.from_device(oa.out), harness.from_device(ob.out))
 
 
 def _worked_example(dtype):
@@ -326,3 +327,53 @@ def test_decode_equals_last_prefill_row():
     torch.cuda.synchronize()
     assert_close(out_f64(out, "bf16")[0], ref[-1], "bf16", "decode vs prefill last row")
     assert_close(out_f64(dp.out, "bf16")[-1], ref[-1], "bf16", "prefill last row")
+
+
+# ---------------------------------------------------------------------------
+# the balanced split (partition_size 0): slices cut across sequence boundaries
+
+BALANCED_CASES = [
+    # dtype, HQ, HKV, D, block_size, context lens (0 = empty row)
+    ("bf16", 16, 8, 128, 256, [0, 1, 2, 15, 16, 17, 0, 300, 4000, 1, 1, 33, 0, 2048, 5]),
+    ("bf16", 14, 2, 64, 16, [1, 0, 7, 2048, 3, 1000, 0, 64, 65, 1]),
+    ("f32", 8, 2, 128, 8, [0, 1, 9, 100, 0, 257]),
+    ("bf16", 32, 2, 128, 16, [5, 0, 1200, 17]),
+    ("bf16", 8, 1, 128, 32, [1] * 40 + [3000]),
+    ("bf16", 16, 8, 128, 256, [8192, 7, 8192]),
+]
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}q{c[2]}kv-d{c[3]}-bs{c[4]}-n{len(c[5])}")
+def test_decode_balanced_mixed_lengths(case):
+    dtype, HQ, HKV, D, bs, lens = case
+    lens = np.array(lens, dtype=np.int32)
+    w = make_workload(name="balanced", kind="decode", dtype=dtype, num_q_heads=HQ,
+                      num_kv_heads=HKV, head_dim=D, block_size=bs, seq_lens_k=np.maximum(lens, 1),
+                      seed=200 + BALANCED_CASES.index(case))
+    announce(f"decode balanced {case[:5]} lens={lens.tolist()[:8]}...")
+    dw = harness.DeviceWorkload(w, "cuda", partition_size=0)
+    dw.load_history()
+    dw.step()
+    ctx = torch.from_numpy(lens).cuda()
+    out = torch.full_like(dw.out, float("nan"))
+    pk.pa_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_table, ctx, w.scale,
+                 max_context_len=int(lens.max()), partition_size=0, workspace=dw.workspace)
+    torch.cuda.synchronize()
+    ref = OracleRun(w)
+    want = oracle.decode(w.q, ref.k_pool, ref.v_pool, w.block_table, lens, w.scale, dtype)
+    assert_close(out_f64(out, dtype), want, dtype, str(case[:5]))
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+def test_decode_two_passes_equal_one_call(partition):
+    """pa_decode_partitions + pa_decode_merge give exactly pa_decode's output."""
+    w = config(1)
+    announce(f"decode two passes vs one call, partition {partition}")
+    dw = run_hip(w, partition_size=partition)
+    out2 = torch.full_like(dw.out, float("nan"))
+    pk.pa_decode_partitions(out2, dw.q, dw.k_cache, dw.v_cache, dw.block_table, dw.seq_lens_k,
+                            w.scale, w.max_seqlen_k, partition, dw.workspace)
+    pk.pa_decode_merge(out2, dw.workspace, dw.seq_lens_k, w.num_kv_heads, w.max_seqlen_k, partition)
+    torch.cuda.synchronize()
+    assert bits_equal(harness.from_device(out2), harness.from_device(dw.out))
