@@ -249,7 +249,7 @@ int pa_decode_merge(void* out, const void* workspace, const int32_t* context_len
  *   cu_seqlens_k in   int32 [num_seqs + 1], Lk >= Lq for every sequence
  *   max_seqlen_q / max_seqlen_k   host upper bounds of Lq / Lk
  *
- * dtype must be PA_BF16 (the matrix-core path).
+ * dtype must be PA_BF16 (the matrix-core path) and scale must be > 0.
  */
 int pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, int32_t max_blocks_per_seq,

@@ -23,8 +23,18 @@ inline int elt_bytes(pa_dtype t) { return t == PA_BF16 ? 2 : 4; }
 
 constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 
+constexpr int kNumXCDs = 8;
+
 // ---------------------------------------------------------------------------
 // Device side.
+
+// Workgroups are handed to the XCDs round-robin in launch order (id % 8).  This maps launch
+// id L of N to a logical id so that each XCD receives one contiguous range of logical ids:
+// XCD x gets ids [x*q + min(x, r), ...) with q = N / 8, r = N % 8 (a bijection on [0, N)).
+__device__ __forceinline__ int xcd_local_id(int L, int N) {
+  const int x = L % kNumXCDs, q = N / kNumXCDs, r = N % kNumXCDs;
+  return x * q + min(x, r) + L / kNumXCDs;
+}
 
 // bf16 <-> fp32.  A bf16 value is the top half of an fp32, so widening is a
 // shift; narrowing rounds to nearest-even (NaN stays NaN).

@@ -277,6 +277,9 @@ PREFILL_CASES = [
     (4, 1, 64, 8, [90], [90]),
     (32, 4, 128, 64, [150, 260], [40, 130]),
     (16, 1, 128, 256, [513], [257]),
+    # block tables longer than the kernel's LDS copy (2048 entries): the window slides
+    (2, 1, 64, 8, [40000, 300], [40, 100]),
+    (8, 2, 128, 8, [18000], [32]),
 ]
 
 
