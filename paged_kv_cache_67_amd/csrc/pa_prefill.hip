@@ -36,22 +36,46 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte regist
 
 constexpr int kPrefillRows = 128;     // query rows (position x head) per workgroup
 constexpr int kPrefillKeys = 64;      // keys per tile
-constexpr int kPrefillThreads = 512;  // 8 waves of 16 rows
+constexpr int kPrefillThreads = 512;  // 8 waves: 4 row groups x 2 key halves
 constexpr int kBtCache = 2048;        // block-table entries of one sequence kept in LDS
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
+// Running max before any unmasked key: finite, so that a masked score (-inf) still gives
+// exp2(-inf - m) = 0 rather than NaN, and a key half that never sees a key merges with weight 0.
+constexpr float kNoMax = -1.0e30f;
 
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Max over the four lanes l, l^16, l^32, l^48 (the lanes that hold one query's scores), on
+// gfx950's lane-swap instructions instead of an LDS round trip.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // v_mfma_f32_16x16x32_bf16 layouts (k index written as (group, i), group = lane / 16):
 //   A[m][k]: lane holds m = lane % 16, k = (group, i = 0..7); B[k][n]: n = lane % 16;
 //   C/D[m][n]: lane holds m = 4 * group + i (i = 0..3), n = lane % 16.
-// S^T = K Q^T per 16-key block kb: lane holds the scores of query lane%16 for keys
-// 16kb + 4*group + i.  For O^T += V^T P^T over 32 keys (step ks), the MFMA k index
-// (group, i) stands for key 32ks + 16*(i/4) + 4*group + i%4 on both operands: P comes
-// straight from S^T blocks 2ks and 2ks+1, V^T from two transposing LDS reads.
-template <int D, int G>
+// Wave w owns 32 query rows, 32*(w%4) + 16*qg + lane%16 for query groups qg = 0, 1, and
+// the 32 keys 32*(w/4) + 0..31 of every 64-key tile (its key half).  Both query groups
+// share every K and V operand read.  S^T = K Q^T per 16-key block kb: lane holds the
+// scores of its query for keys 16kb + 4*group + i of the half.  For O^T += V^T P^T over
+// the half's 32 keys, the MFMA k index (group, i) stands for key 16*(i/4) + 4*group + i%4
+// on both operands: P comes straight from blocks kb = 0, 1, V^T from two transposing LDS
+// reads.  The row sums l come from one more MFMA with an all-ones A operand, so they are
+// summed from the same bf16 probabilities as the numerator.  The two key halves of a row
+// keep separate (m, l, O) and are merged through LDS at the end.
+//
+// Pipeline: iteration t holds S_t in registers, computes S_{t+1} from K tile t+1 while it
+// exponentiates S_t, then accumulates V tile t.  K therefore runs one tile ahead of V in
+// LDS and in the loads: at the end of iteration t the register set R (B for even t, A for
+// odd) holds K_{t+2} and V_{t+1}, is written to LDS, and is refilled with K_{t+4} and
+// V_{t+3}.  WIDE (block_size >= 64): every tile lies inside one block, so a tile's address
+// is a scalar base plus a per-lane offset that does not change from tile to tile.
+template <int D, int G, bool WIDE>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_table, int maxb,
@@ -60,14 +84,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   constexpr int BM = kPrefillRows / G;  // positions per workgroup
   constexpr int BN = kPrefillKeys;
   constexpr int NT = kPrefillThreads;
-  constexpr int KP = D + 8;    // K row pitch (bf16): 68 words for D=128
-  constexpr int VP = D + 16;   // V row pitch (bf16): 72 words for D=128
-  constexpr int DS = D / 32;   // 32-wide d steps of S^T
-  constexpr int DB = D / 16;   // 16-wide d blocks of O^T
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int P = D + 16;   // K and V row pitch (bf16); conflict-free for both LDS reads
+  constexpr int DS = D / 32;  // 32-wide d steps of S^T
+  constexpr int DB = D / 16;  // 16-wide d blocks of O^T
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int LPT = BN * CPR / NT;  // 16-byte loads per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * VP];
+  // K tiles in buffers 0, 1 and V tiles in 2, 3; after the loop the same memory carries
+  // the key-half partial results (4 x 2 x 32 x 64 floats of O, then m and l).
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[4][BN * P];
+  static_assert(sizeof(sKV) >= (4 * 2 * (4 * DB + 2) * 64) * sizeof(float), "merge area");
   __shared__ int s_bt[kBtCache];
   __shared__ int s_bad;
 
@@ -89,22 +114,53 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int qc = lane & 15, grp = lane >> 4;
-  const int row = 16 * w + qc;
-  const int rpos = row / G, rhead = row % G;
-  const int64_t qtok = (int64_t)q0 + pos0 + rpos;
-  const bool rvalid = row < BM * G && rpos < npos && qtok >= 0 && qtok < total_q;
-  const int h = g * G + rhead;
-  const int row_nk = (causal && rvalid) ? prefix + pos0 + rpos + 1 : nk;
+  const int rg = w & 3;  // row group
+  const int kh = w >> 2;  // key half
+  int64_t qtok[2];
+  bool rvalid[2];
+  int hq[2], row_nk[2];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    const int row = 32 * rg + 16 * qg + qc;
+    const int rpos = row / G;
+    qtok[qg] = (int64_t)q0 + pos0 + rpos;
+    rvalid[qg] = row < BM * G && rpos < npos && qtok[qg] >= 0 && qtok[qg] < total_q;
+    hq[qg] = g * G + row % G;
+    row_nk[qg] = (causal && rvalid[qg]) ? prefix + pos0 + rpos + 1 : nk;
+  }
   const int nk_min = causal ? min(nk, prefix + pos0 + 1) : nk;
   const int bs_mask = (1 << bs_log2) - 1;
+  const int HKVD = HKV * D;  // elements between consecutive tokens of a block
   const int32_t* bt = block_table + (int64_t)b * maxb;
 
-  // s_bt[i] caches block-table entry btb + i for i < min(nblk - btb, kBtCache).  Block ids
-  // are read only from LDS inside the key loop: a global read there would make each tile's
-  // address computation wait for every K/V load still in flight.
-  const int nblk = min(nk > 0 ? ((nk - 1) >> bs_log2) + 1 : 0, maxb);
+  bf16x8_t qreg[2][DS];  // B operand of S^T: this lane's queries, d = 32ds + 8*grp + 0..7
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rvalid[qg])
+        v = *reinterpret_cast<const uint4*>(q + (qtok[qg] * HQ + hq[qg]) * D + 32 * ds + 8 * grp);
+      qreg[qg][ds] = __builtin_bit_cast(bf16x8_t, v);
+    }
+
+  // s_bt[i] holds block-table entry btb + i for i < nv = min(nblk - btb, kBtCache), each
+  // checked against the pool when loaded (a bad id marks the output and reads block 0).
+  // Block ids are read only from LDS inside the key loop: a global read there would make
+  // each tile's address computation wait for every K/V load still in flight.
+  const int nblk_need = nk > 0 ? ((nk - 1) >> bs_log2) + 1 : 0;
+  const int nblk = min(nblk_need, maxb);
+  int bad = nblk_need > maxb;
   int btb = 0;
-  for (int i = tid; i < min(nblk, kBtCache); i += NT) s_bt[i] = bt[i];
+  auto fill = [&]() __attribute__((always_inline)) {
+    for (int i = tid; i < min(nblk - btb, kBtCache); i += NT) {
+      const int v = bt[btb + i];
+      const bool ok = v >= 0 && v < num_blocks;
+      bad |= !ok;
+      s_bt[i] = ok ? v : 0;
+    }
+  };
+  fill();
   if (tid == 0) s_bad = 0;
   __syncthreads();
   // Slides the window to start at the block of key kt when the keys [kt, kt + BN) run past
@@ -114,181 +170,255 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     if (((min(kt + BN, nk) - 1) >> bs_log2) >= btb + kBtCache) {
       __syncthreads();
       btb = min(kt, nk - 1) >> bs_log2;
-      for (int i = tid; i < min(nblk - btb, kBtCache); i += NT) s_bt[i] = bt[btb + i];
+      fill();
       __syncthreads();
     }
   };
-
-  bf16x8_t qreg[DS];  // B operand of S^T: this lane's query, d = 32ds + 8*grp + 0..7
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rvalid) v = *reinterpret_cast<const uint4*>(q + (qtok * HQ + h) * D + 32 * ds + 8 * grp);
-    qreg[ds] = __builtin_bit_cast(bf16x8_t, v);
-  }
-
-  // K/V tiles travel global -> registers -> LDS.  Two register sets (A, B) alternate so a
-  // tile's loads are issued two iterations before its LDS store needs them.
-  int bad = 0;
-  u32x4_t rkA[LPT], rvA[LPT], rkB[LPT], rvB[LPT];
-  auto load_tile = [&](int kt, u32x4_t (&rk)[LPT], u32x4_t (&rv)[LPT])
-                       __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + NT * i;
-      const int j = min(kt + c / CPR, nk - 1);
-      const int jb = j >> bs_log2;
-      // jb - btb lies in [0, kBtCache) after cover(kt); an entry past the cached ones is read
-      // only when jb >= maxb, which marks the tile bad whatever it holds.
-      int blk = s_bt[min(max(jb - btb, 0), kBtCache - 1)];
-      const bool ok = jb < maxb && blk >= 0 && blk < num_blocks;
-      bad |= !ok;
-      blk = ok ? blk : 0;
-      const int64_t off = ((((int64_t)blk << bs_log2) + (j & bs_mask)) * HKV + g) * D + (c % CPR) * 8;
-      rk[i] = *reinterpret_cast<const u32x4_t*>(kc + off);
-      rv[i] = *reinterpret_cast<const u32x4_t*>(vc + off);
-    }
-  };
-  auto store_tile = [&](int buf, const u32x4_t (&rk)[LPT], const u32x4_t (&rv)[LPT])
-                        __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + NT * i;
-      *reinterpret_cast<u32x4_t*>(&sK[buf][(c / CPR) * KP + (c % CPR) * 8]) = rk[i];
-      *reinterpret_cast<u32x4_t*>(&sV[buf][(c / CPR) * VP + (c % CPR) * 8]) = rv[i];
-    }
+  // Entry 0 always holds a checked id (nblk >= 1 whenever there is a tile), so the clamp
+  // keeps every read on a loaded entry; a key past the table (jb >= maxb) is already bad.
+  auto lookup = [&](int jb) __attribute__((always_inline)) {
+    return s_bt[max(min(jb - btb, min(nblk - btb, kBtCache) - 1), 0)];
   };
 
-  f32x4_t o[DB];
+  // Thread tid moves 16-byte chunks c = tid + NT*i of a tile: key row c / CPR, d chunk c % CPR.
+  int trow[LPT], tcol[LPT];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, l = 0.0f;
-
-  // Transposing read: lane p = a + 4t of group grp addresses key 4*grp + t (+32ks, +16 for
-  // the second half) at d column 4a (+16db); lane 4a + c then holds d = 16db + 4a + c.
-  const int tr_row = 4 * grp + ((lane & 15) >> 2);
-  const int tr_col = 4 * (lane & 3);
-
-  // Every path through the prologue and the loop issues the same loads in the same order
-  // (a tile start of nk, past the last tile, loads key nk - 1 and is never stored), so the
-  // compiler's wait counts stay exact: storing one register set waits for that set only.
-  if (ntiles > 0) {
-    load_tile(0, rkA, rvA);
-    const int kt1 = ntiles > 1 ? BN : nk;
-    cover(kt1);
-    load_tile(kt1, rkB, rvB);
-    store_tile(0, rkA, rvA);
-    const int kt2 = ntiles > 2 ? 2 * BN : nk;
-    cover(kt2);
-    load_tile(kt2, rkA, rvA);
+  for (int i = 0; i < LPT; ++i) {
+    trow[i] = (tid + NT * i) / CPR;
+    tcol[i] = g * D + ((tid + NT * i) % CPR) * 8;
   }
-  // Settle the Q loads here, behind the tile loads issued after them: otherwise the wait
-  // for them lands in the loop header as a full drain of every load in flight.
+  // A tile start of nk or more (past the last tile) loads key nk - 1 and is never used.
+  int64_t off[LPT];  // general path: element offsets of the K tile loaded last
+  auto tile_offsets = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+v"(qreg[ds]));
-  __syncthreads();
-
-  // Iteration t computes tile t from LDS buffer t&1, moves tile t+1 from registers R into
-  // the other buffer and refills R with tile t+3; R alternates B, A, B, ...
-  auto step = [&](int t, u32x4_t (&rk)[LPT], u32x4_t (&rv)[LPT]) __attribute__((always_inline)) {
-    const int kt = t * BN;
-    const uint16_t* K = sK[t & 1];
-    const uint16_t* V = sV[t & 1];
-
-    f32x4_t s[4];
+    for (int i = 0; i < LPT; ++i) {
+      const int j = min(kt + trow[i], nk - 1);
+      off[i] = (int64_t)lookup(j >> bs_log2) * ((int64_t)HKVD << bs_log2) +
+               (int)((j & bs_mask) * HKVD + tcol[i]);
+    }
+  };
+  auto load_wide = [&](const uint16_t* src, int kt, u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
+    const int ktc = min(kt, (ntiles - 1) * BN);
+    const int blk = __builtin_amdgcn_readfirstlane(lookup(ktc >> bs_log2));
+    const uint16_t* base = src + (((int64_t)blk << bs_log2) + (ktc & bs_mask)) * HKVD;
+    const int lim = nk - 1 - ktc;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < LPT; ++i)
+      r[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) +
+                                               (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])));
+  };
+  auto load_k = [&](int kt, u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
+    cover(kt);
+    if constexpr (WIDE) {
+      load_wide(kc, kt, r);
+    } else {
+      tile_offsets(kt);
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(kc + off[i]);
+    }
+  };
+  // V tile kt always follows the K load of the same tile (no window move in between); the
+  // general path reuses that load's offsets.
+  auto load_v = [&](int kt, u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
+    if constexpr (WIDE) {
+      load_wide(vc, kt, r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(vc + off[i]);
+    }
+  };
+  auto store = [&](uint16_t* dst, const u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      *reinterpret_cast<u32x4_t*>(dst + trow[i] * P + (tcol[i] - g * D)) = r[i];
+  };
+  const int krow = 32 * kh + qc;  // K operand row of block kb = 0 in this wave's key half
+  auto scores = [&](const uint16_t* K, f32x4_t (&s)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[0][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      s[1][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
         const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(&K[(16 * kb + qc) * KP + 32 * ds + 8 * grp]);
-        s[kb] = mfma16(a, qreg[ds], s[kb]);
+            *reinterpret_cast<const bf16x8_t*>(&K[(krow + 16 * kb) * P + 32 * ds + 8 * grp]);
+        s[0][kb] = mfma16(a, qreg[0][ds], s[0][kb]);
+        s[1][kb] = mfma16(a, qreg[1][ds], s[1][kb]);
       }
     }
+  };
 
+  f32x4_t o[2][DB];
+  f32x4_t lsum[2];
+  float m[2];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[qg][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    lsum[qg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    m[qg] = kNoMax;
+  }
+  bf16x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+
+  // Transposing read: lane p = a + 4t of group grp addresses key 4*grp + t (+16 for the
+  // second half) of the key half at d column 4a (+16db); lane 4a + c then holds
+  // d = 16db + 4a + c.
+  const int tr_off = (32 * kh + 4 * grp + ((lane & 15) >> 2)) * P + 4 * (lane & 3);
+
+  u32x4_t rkA[LPT], rvA[LPT], rkB[LPT], rvB[LPT];
+  f32x4_t sc[2][2];  // scores of the tile being reduced
+  // Every path issues the same loads in the same order, so the compiler's wait counts stay
+  // exact: writing one register set to LDS waits for that set only.
+  auto step = [&](int t, u32x4_t (&rk)[LPT], u32x4_t (&rv)[LPT]) __attribute__((always_inline)) {
+    const int kt = t * BN;
     if (kt + BN > nk_min) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt + 16 * kb + 4 * grp + i;
-          s[kb][i] = key < row_nk ? s[kb][i] : -INFINITY;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt + 32 * kh + 16 * kb + 4 * grp + i;
+            sc[qg][kb][i] = key < row_nk[qg] ? sc[qg][kb][i] : -INFINITY;
+          }
     }
-    float mx = -INFINITY;
+    float mx[2];
+    bool grow[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qg = 0; qg < 2; ++qg) {
+      mx[qg] = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-    const bool grow = mx > m + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float alpha = grow ? fast_exp2(m - mx) : 1.0f;
-      m = grow ? mx : m;
-      l *= alpha;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int i = 0; i < 4; ++i) mx[qg] = fmaxf(mx[qg], sc[qg][kb][i]);
+      mx[qg] = max_over_groups(mx[qg]) * scale_log2;
+      grow[qg] = mx[qg] > m[qg] + kLazyRescale;
     }
+    if (__builtin_amdgcn_ballot_w64(grow[0] || grow[1])) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int qg = 0; qg < 2; ++qg) {
+        const float alpha = grow[qg] ? fast_exp2(m[qg] - mx[qg]) : 1.0f;
+        m[qg] = grow[qg] ? mx[qg] : m[qg];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m));
-        s[kb][i] = p;
-        l += p;
-      }
-
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (__bf16)s[2 * ks][i];
-        pb[4 + i] = (__bf16)s[2 * ks + 1][i];
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint16_t* base = V + (32 * ks + tr_row) * VP + 16 * db + tr_col;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (v4i16_t __attribute__((address_space(3)))*)(base));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (v4i16_t __attribute__((address_space(3)))*)(base + 16 * VP));
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = mfma16(a, pb, o[db]);
+        for (int db = 0; db < DB; ++db) o[qg][db] *= alpha;
+        lsum[qg] *= alpha;
       }
     }
 
-    if (t + 1 < ntiles) store_tile((t + 1) & 1, rk, rv);
-    const int kn = t + 3 < ntiles ? kt + 3 * BN : nk;
-    cover(kn);
-    load_tile(kn, rk, rv);
+    f32x4_t sn[2][2];
+    scores(sKV[(t + 1) & 1], sn);
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[qg][i] = (__bf16)fast_exp2(fmaf(sc[qg][0][i], scale_log2, -m[qg]));
+        pb[qg][4 + i] = (__bf16)fast_exp2(fmaf(sc[qg][1][i], scale_log2, -m[qg]));
+      }
+
+    const uint16_t* V = sKV[2 + (t & 1)] + tr_off;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (v4i16_t __attribute__((address_space(3)))*)(V + 16 * db));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (v4i16_t __attribute__((address_space(3)))*)(V + 16 * db + 16 * P));
+      const bf16x8_t a =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[0][db] = mfma16(a, pb[0], o[0][db]);
+      o[1][db] = mfma16(a, pb[1], o[1][db]);
+    }
+    lsum[0] = mfma16(ones, pb[0], lsum[0]);
+    lsum[1] = mfma16(ones, pb[1], lsum[1]);
+
+    // K_{t+2} into the K buffer read last iteration, V_{t+1} into the V buffer read last
+    // iteration (stale tiles past the end are written but never read).
+    store(sKV[t & 1], rk);
+    store(sKV[2 + ((t + 1) & 1)], rv);
+    load_v(t + 3 < ntiles ? kt + 3 * BN : nk, rv);
+    load_k(t + 4 < ntiles ? kt + 4 * BN : nk, rk);
     __syncthreads();
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+      sc[qg][0] = sn[qg][0];
+      sc[qg][1] = sn[qg][1];
+    }
   };
+
   if (ntiles > 0) {
-    for (int t = 0;; t += 2) {
+    // Prologue: K_0, K_1, V_0 into LDS; B = (K_2, V_1), A = (K_3, V_2) in flight.
+    load_k(0, rkA);
+    load_v(0, rvA);
+    load_k(ntiles > 1 ? BN : nk, rkB);
+    load_v(ntiles > 1 ? BN : nk, rvB);
+    store(sKV[0], rkA);
+    store(sKV[2], rvA);
+    store(sKV[1], rkB);
+    load_k(ntiles > 2 ? 2 * BN : nk, rkB);
+    load_v(ntiles > 2 ? 2 * BN : nk, rvA);
+    load_k(ntiles > 3 ? 3 * BN : nk, rkA);
+    // Settle the Q loads here, behind the tile loads issued after them: otherwise the wait
+    // for them lands in the loop header as a full drain of every load in flight.
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+v"(qreg[qg][ds]));
+    __syncthreads();
+    scores(sKV[0], sc);
+    __syncthreads();  // iteration 0 overwrites buffer 0
+    // Two steps per trip and no exit between them: an exit there lets the compiler sink
+    // the first step's loads past it, and the wait counts at the loop header turn into
+    // full drains.  With an odd tile count the last step runs past the end, where every
+    // key is masked and it adds nothing.
+    for (int t = 0; t < ntiles; t += 2) {
       step(t, rkB, rvB);
-      if (t + 1 >= ntiles) break;
       step(t + 1, rkA, rvA);
-      if (t + 2 >= ntiles) break;
     }
   }
 
+  // Merge the key halves: waves 4..7 publish (m, l, O) of their rows, waves 0..3 combine.
+  // The loop ended on a barrier, so the tile buffers are free.
   if (bad) s_bad = 1;
-  __syncthreads();
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  const float inv = s_bad ? NAN : 1.0f / l;
-  if (!rvalid) return;
-  uint16_t* dst = out + (qtok * HQ + h) * D;
+  float* mO = reinterpret_cast<float*>(&sKV[0][0]);
+  float* mM = mO + 4 * 2 * 4 * DB * 64;
+  float* mL = mM + 4 * 2 * 64;
+  if (kh == 1) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    uint2 pk;
-    pk.x = uint32_t(f32_to_bf16(o[db][0] * inv)) | (uint32_t(f32_to_bf16(o[db][1] * inv)) << 16);
-    pk.y = uint32_t(f32_to_bf16(o[db][2] * inv)) | (uint32_t(f32_to_bf16(o[db][3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(dst + 16 * db + 4 * grp) = pk;
+    for (int qg = 0; qg < 2; ++qg) {
+      const int rq = (rg * 2 + qg) * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mO[((rg * 2 + qg) * 4 * DB + 4 * db + i) * 64 + lane] = o[qg][db][i];
+      mM[rq] = m[qg];
+      mL[rq] = lsum[qg][0];
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const bool poisoned = s_bad != 0;
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    const int rq = (rg * 2 + qg) * 64 + lane;
+    const float m1 = mM[rq];
+    const float mm = fmaxf(m[qg], m1);
+    const float a0 = fast_exp2(m[qg] - mm), a1 = fast_exp2(m1 - mm);
+    const float inv = poisoned ? NAN : 1.0f / (lsum[qg][0] * a0 + mL[rq] * a1);
+    if (!rvalid[qg]) continue;
+    uint16_t* dst = out + (qtok[qg] * HQ + hq[qg]) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      float r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = (o[qg][db][i] * a0 + mO[((rg * 2 + qg) * 4 * DB + 4 * db + i) * 64 + lane] * a1) * inv;
+      uint2 pk;
+      pk.x = uint32_t(f32_to_bf16(r[0])) | (uint32_t(f32_to_bf16(r[1])) << 16);
+      pk.y = uint32_t(f32_to_bf16(r[2])) | (uint32_t(f32_to_bf16(r[3])) << 16);
+      *reinterpret_cast<uint2*>(dst + 16 * db + 4 * grp) = pk;
+    }
   }
 }
 
@@ -296,18 +426,18 @@ typedef void (*prefill_fn)(uint16_t*, const uint16_t*, const uint16_t*, const ui
                            const int32_t*, int, const int32_t*, const int32_t*, int, int, int, int,
                            int, float, int);
 
-template <int D>
+template <int D, bool WIDE>
 static prefill_fn pick_prefill_g(int G) {
   switch (G) {
-    case 1: return prefill_kernel<D, 1>;
-    case 2: return prefill_kernel<D, 2>;
-    case 3: return prefill_kernel<D, 3>;
-    case 4: return prefill_kernel<D, 4>;
-    case 5: return prefill_kernel<D, 5>;
-    case 6: return prefill_kernel<D, 6>;
-    case 7: return prefill_kernel<D, 7>;
-    case 8: return prefill_kernel<D, 8>;
-    case 16: return prefill_kernel<D, 16>;
+    case 1: return prefill_kernel<D, 1, WIDE>;
+    case 2: return prefill_kernel<D, 2, WIDE>;
+    case 3: return prefill_kernel<D, 3, WIDE>;
+    case 4: return prefill_kernel<D, 4, WIDE>;
+    case 5: return prefill_kernel<D, 5, WIDE>;
+    case 6: return prefill_kernel<D, 6, WIDE>;
+    case 7: return prefill_kernel<D, 7, WIDE>;
+    case 8: return prefill_kernel<D, 8, WIDE>;
+    case 16: return prefill_kernel<D, 16, WIDE>;
   }
   return nullptr;
 }
@@ -340,6 +470,9 @@ extern "C" int pa_prefill_paged(void* out, const void* q, const void* k_cache, c
   if (!(scale > 0.0f)) return fail(PA_ERR_SHAPE, "pa_prefill_paged: scale must be > 0");
   if (num_blocks == 0 && total_q > 0)
     return fail(PA_ERR_SHAPE, "pa_prefill_paged: empty pool");
+  if ((int64_t)block_size * num_kv_heads * head_dim >= (int64_t)1 << 31)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_paged: block of %d x %d x %d elements too large",
+                block_size, num_kv_heads, head_dim);
   if (max_seqlen_q > max_seqlen_k)
     return fail(PA_ERR_SHAPE, "pa_prefill_paged: max_seqlen_q %d > max_seqlen_k %d", max_seqlen_q,
                 max_seqlen_k);
@@ -349,7 +482,9 @@ extern "C" int pa_prefill_paged(void* out, const void* q, const void* k_cache, c
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_ALIGN, "pa_prefill_paged: pointers must be 16-byte aligned");
   const int G = num_q_heads / num_kv_heads;
-  prefill_fn fn = head_dim == 64 ? pick_prefill_g<64>(G) : pick_prefill_g<128>(G);
+  const bool wide = block_size >= kPrefillKeys;
+  prefill_fn fn = head_dim == 64 ? (wide ? pick_prefill_g<64, true>(G) : pick_prefill_g<64, false>(G))
+                                 : (wide ? pick_prefill_g<128, true>(G) : pick_prefill_g<128, false>(G));
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_paged: GQA group %d (1-8 or 16)", G);
   const int BM = kPrefillRows / G;
   dim3 grid((max_seqlen_q + BM - 1) / BM, num_kv_heads, num_seqs);
