@@ -94,6 +94,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sKV[4][BN * P];
   static_assert(sizeof(sKV) >= (4 * 2 * (4 * DB + 2) * 64) * sizeof(float), "merge area");
   __shared__ int s_bt[kBtCache];
+  static_assert(kBtCache % NT == 0, "block-table window split over the threads");
   __shared__ int s_bad;
 
   // Consecutive logical ids (query tiles of one sequence and KV head) share an XCD, so the
@@ -101,9 +102,20 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   const int nx = gridDim.x, ny = gridDim.y;
   const int lid = xcd_local_id(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
   const int qt = lid % nx, g = (lid / nx) % ny, b = lid / (nx * ny);
-  const int q0 = cu_q[b];
-  const int Lq = cu_q[b + 1] - q0;
-  const int Lk = cu_k[b + 1] - cu_k[b];
+  const int tid = threadIdx.x;
+  const int32_t* bt = block_table + (int64_t)b * maxb;
+  // The first kBtCache block-table entries are fetched before the sequence lengths arrive
+  // (they depend only on the sequence index), so the two loads overlap; they are checked
+  // and kept once the lengths say how many are used.
+  constexpr int BTPT = kBtCache / NT;
+  int braw[BTPT];
+#pragma unroll
+  for (int i = 0; i < BTPT; ++i) braw[i] = tid + NT * i < maxb ? bt[tid + NT * i] : 0;
+  // Both offset pairs are read before any of them is used (one round trip, not two).
+  int q0 = cu_q[b], q1 = cu_q[b + 1], k0 = cu_k[b], k1 = cu_k[b + 1];
+  asm volatile("" : "+s"(q0), "+s"(q1), "+s"(k0), "+s"(k1));
+  const int Lq = q1 - q0;
+  const int Lk = k1 - k0;
   const int pos0 = qt * BM;
   if (pos0 >= Lq) return;
   const int npos = min(BM, Lq - pos0);
@@ -111,7 +123,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   const int nk = causal ? min(Lk, prefix + pos0 + npos) : Lk;
   const int ntiles = nk > 0 ? (nk + BN - 1) / BN : 0;
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int qc = lane & 15, grp = lane >> 4;
   const int rg = w & 3;  // row group
@@ -131,18 +142,19 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   const int nk_min = causal ? min(nk, prefix + pos0 + 1) : nk;
   const int bs_mask = (1 << bs_log2) - 1;
   const int HKVD = HKV * D;  // elements between consecutive tokens of a block
-  const int32_t* bt = block_table + (int64_t)b * maxb;
 
-  bf16x8_t qreg[2][DS];  // B operand of S^T: this lane's queries, d = 32ds + 8*grp + 0..7
+  // B operand of S^T: this lane's queries, d = 32ds + 8*grp + 0..7.  A row past the
+  // sequence reads a clamped (valid) token instead: rows never mix and such a row is not
+  // stored, and unconditional loads keep the compiler from draining the queue after each.
+  bf16x8_t qreg[2][DS];
 #pragma unroll
-  for (int qg = 0; qg < 2; ++qg)
+  for (int qg = 0; qg < 2; ++qg) {
+    const int64_t tok = min(max(qtok[qg], (int64_t)0), (int64_t)total_q - 1);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (rvalid[qg])
-        v = *reinterpret_cast<const uint4*>(q + (qtok[qg] * HQ + hq[qg]) * D + 32 * ds + 8 * grp);
-      qreg[qg][ds] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int ds = 0; ds < DS; ++ds)
+      qreg[qg][ds] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const uint4*>(q + (tok * HQ + hq[qg]) * D + 32 * ds + 8 * grp));
+  }
 
   // s_bt[i] holds block-table entry btb + i for i < nv = min(nblk - btb, kBtCache), each
   // checked against the pool when loaded (a bad id marks the output and reads block 0).
@@ -160,7 +172,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
       s_bt[i] = ok ? v : 0;
     }
   };
-  fill();
+#pragma unroll
+  for (int i = 0; i < BTPT; ++i) {
+    if (tid + NT * i < min(nblk, kBtCache)) {
+      const bool ok = braw[i] >= 0 && braw[i] < num_blocks;
+      bad |= !ok;
+      s_bt[tid + NT * i] = ok ? braw[i] : 0;
+    }
+  }
   if (tid == 0) s_bad = 0;
   __syncthreads();
   // Slides the window to start at the block of key kt when the keys [kt, kt + BN) run past
