@@ -259,6 +259,46 @@ int pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* 
                      int32_t num_kv_heads, int32_t head_dim, float scale, int32_t causal,
                      pa_dtype dtype, void* stream);
 
+/*
+ * pa_mixed_workspace_size -- bytes of workspace pa_attention_mixed needs.
+ *
+ * For num_seqs sequences (at most 4096) whose key counts are at most
+ * max_seqlen_k; 0 for invalid sizes.  The layout is the balanced split's of
+ * pa_decode (per query head and slice two partial states, then the chunk
+ * prefix sums), covering the batch's decode rows.
+ */
+size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_seqlen_k);
+
+/*
+ * pa_attention_mixed -- one launch for a batch that mixes prompt chunks and
+ * decode rows.
+ *
+ * Arguments and result are those of pa_prefill_paged with causal = 1: query
+ * i of sequence b (Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] queries,
+ * Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys) sits at position Lk - Lq + i
+ * and attends keys 0 .. Lk - Lq + i ([KVblog] 3.5; [Lab] B.6).  A sequence
+ * with Lq = 1 is a decode row ([mini] section 5: its one query attends all Lk
+ * keys); such rows take the split-K decode path and the others the matrix-core
+ * prefill path, inside the same launch, followed by a small merge launch on
+ * the same stream.  A decode row with Lk = 0 gives a zero row.
+ *
+ *   workspace    scratch of pa_mixed_workspace_size(num_seqs, num_q_heads,
+ *                num_kv_heads, head_dim, max_seqlen_k) bytes, 16-byte aligned,
+ *                owned by the caller; no initialisation needed
+ *
+ * dtype must be PA_BF16, scale > 0, num_seqs <= 4096, num_q_heads/num_kv_heads
+ * in 1..8 or 16.  Errors as for pa_prefill_paged, plus PA_ERR_WORKSPACE for a
+ * missing or short workspace.
+ */
+int pa_attention_mixed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                       int32_t max_seqlen_k, int32_t num_blocks, int32_t block_size,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+                       pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

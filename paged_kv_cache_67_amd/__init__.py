@@ -13,11 +13,13 @@ from ._binding import (  # noqa: F401
     PAError,
     lib,
     lib_path,
+    pa_attention_mixed,
     pa_decode,
     pa_decode_merge,
     pa_decode_partitions,
     pa_decode_workspace_size,
     pa_last_error,
+    pa_mixed_workspace_size,
     pa_prefill_paged,
     pa_slot_mapping,
     pa_status_string,

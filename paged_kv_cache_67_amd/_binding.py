@@ -38,6 +38,10 @@ SIGNATURES = {
     "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pa_prefill_paged": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                    _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int, _vp]),
+    "pa_mixed_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_attention_mixed": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp, _sz,
+                                     _vp]),
 }
 
 
@@ -196,3 +200,25 @@ def pa_prefill_paged(out, q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seq
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k), NB, BS,
         HQ, HKV, D, float(scale), 1 if causal else 0, _dtype(q), _stream(stream)))
+
+
+def pa_mixed_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seqlen_k) -> int:
+    return lib().pa_mixed_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seqlen_k)
+
+
+def pa_attention_mixed(out, q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seqlens_k,
+                       max_seqlen_q, max_seqlen_k, scale, workspace, stream=None):
+    T, HQ, D = q.shape
+    NB, BS, HKV, Dk = k_cache.shape
+    B = block_table.shape[0]
+    assert out.shape == q.shape and Dk == D and v_cache.shape == k_cache.shape
+    assert q.is_contiguous() and out.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
+    assert out.dtype == q.dtype == k_cache.dtype == v_cache.dtype
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    _i32_vec(cu_seqlens_q, B + 1, "cu_seqlens_q")
+    _i32_vec(cu_seqlens_k, B + 1, "cu_seqlens_k")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_attention_mixed", lib().pa_attention_mixed(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k), NB, BS,
+        HQ, HKV, D, float(scale), _dtype(q), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -99,6 +99,19 @@ class DeviceWorkload:
                                 self.cu_q, self.cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
                                 causal=True, stream=stream)
 
+    def attention_mixed(self, stream=None):
+        """The whole batch in one launch: its one-query sequences take the decode
+        path and the others the prefill path (pa_attention_mixed)."""
+        w = self.w
+        if getattr(self, "mixed_workspace", None) is None:
+            nbytes = pa.pa_mixed_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                                w.head_dim, max(1, w.max_seqlen_k))
+            self.mixed_workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32,
+                                               device=self.device)
+        pa.pa_attention_mixed(self.out, self.q, self.k_cache, self.v_cache, self.block_table,
+                              self.cu_q, self.cu_k, max(1, w.max_seqlen_q), max(1, w.max_seqlen_k),
+                              w.scale, self.mixed_workspace, stream=stream)
+
     def step(self, stream=None):
         self.slot_mapping(stream)
         self.store(stream)

@@ -37,6 +37,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for must in ("pa_slot_mapping", "pa_store_kv", "pa_decode", "pa_decode_merge",
                  "pa_prefill_paged", "pa_decode_workspace_size", "pa_decode_partitions",
+                 "pa_attention_mixed", "pa_mixed_workspace_size",
                  "pa_status_string", "pa_last_error", "pa_version"):
         assert must in names
 
@@ -77,6 +78,17 @@ def test_null_and_shape_errors(L):
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 0, None) == 3
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 9, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 1, None) == 2
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 1, None) == 1
+    # pa_attention_mixed: bf16 only, supported groups, batch limit, null checks; empty is a no-op
+    mixed = lambda seqs, tq, mq, mk, hq, hkv, d, dt: L.pa_attention_mixed(
+        None, None, None, None, None, 4, None, None, seqs, tq, mq, mk, 8, 16, hq, hkv, d, 0.1, dt,
+        None, 0, None)
+    assert mixed(2, 8, 4, 8, 4, 2, 128, 0) == 3
+    assert mixed(2, 8, 4, 8, 3, 2, 128, 1) == 2
+    assert mixed(2, 8, 4, 8, 12, 1, 128, 1) == 3     # group 12 has no kernel
+    assert mixed(5000, 8, 4, 8, 4, 2, 128, 1) == 3   # more sequences than the LDS scan holds
+    assert mixed(2, 9, 4, 8, 4, 2, 128, 1) == 2      # total_q > num_seqs * max_seqlen_q
+    assert mixed(2, 8, 4, 8, 4, 2, 128, 1) == 1
+    assert mixed(0, 0, 4, 8, 4, 2, 128, 1) == 0
 
 
 def _gpu_visible():
@@ -102,6 +114,11 @@ def test_alignment_and_workspace_errors(L):
     assert L.pa_decode_partitions(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, -1, a, need, None) == 5
     assert L.pa_decode_partitions(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 128, a, need, None) == 3
     assert L.pa_decode_partitions(None, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, a, need0, None) == 1
+    # the mixed launch always needs its workspace, 16-byte aligned
+    needm = L.pa_mixed_workspace_size(2, 4, 2, 128, 64)
+    assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, 2, 8, 4, 64, 8, 16, 4, 2, 128, 0.1, 1, None, 0, None) == 5
+    assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, 2, 8, 4, 64, 8, 16, 4, 2, 128, 0.1, 1, a, needm - 4, None) == 5
+    assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, 2, 8, 4, 64, 8, 16, 4, 2, 128, 0.1, 1, mis, needm, None) == 4
 
 
 def test_workspace_size_closed_form(L):
@@ -116,3 +133,6 @@ def test_workspace_size_closed_form(L):
     # W is capped by the number of chunks there can be (fp32 d64 chunk: 16 tokens)
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 0) == 2 * 6 * 2 * 66 * 4 + 3 * 4
     assert L.pa_decode_workspace_size(2, 3, 2, 64, 33, 0) == 0     # invalid head ratio
+    # the mixed launch uses the balanced bf16 layout over all its sequences
+    assert L.pa_mixed_workspace_size(264, 16, 8, 128, 4096) == 16 * 256 * 2 * 130 * 4 + 265 * 4
+    assert L.pa_mixed_workspace_size(5000, 16, 8, 128, 4096) == 0

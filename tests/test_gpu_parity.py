@@ -380,3 +380,77 @@ def test_decode_two_passes_equal_one_call(partition):
     pk.pa_decode_merge(out2, dw.workspace, dw.seq_lens_k, w.num_kv_heads, w.max_seqlen_k, partition)
     torch.cuda.synchronize()
     assert bits_equal(harness.from_device(out2), harness.from_device(dw.out))
+
+
+# ---------------------------------------------------------------------------
+# Mixed batches: prompt chunks and decode rows (Lq = 1) in one launch
+
+MIXED_CASES = [
+    # HQ, HKV, D, block_size, seq_lens_k, new_lens
+    (16, 8, 128, 256, [1280, 700, 1, 4000, 257, 1000 + 256, 33], [256, 1, 1, 1, 1, 256, 33]),
+    (16, 8, 128, 16, [620, 33, 17, 1, 2048, 65, 300], [108, 1, 1, 1, 1, 65, 0]),
+    (14, 2, 64, 16, [300, 5, 129, 2048, 7], [100, 1, 129, 1, 1]),   # group 7
+    (32, 2, 128, 64, [150, 260, 3, 90], [40, 1, 1, 90]),              # group 16
+    (4, 1, 64, 8, [90, 40, 1, 17000], [90, 1, 1, 1]),                 # table past the LDS window
+]
+
+
+def _mixed_run(w):
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    dw.slot_mapping()
+    dw.store()
+    dw.attention_mixed()
+    torch.cuda.synchronize()
+    return dw
+
+
+@pytest.mark.parametrize("case", MIXED_CASES, ids=lambda c: f"{c[0]}q{c[1]}kv-d{c[2]}-bs{c[3]}")
+def test_mixed_matches_oracle(case):
+    HQ, HKV, D, bs, lk, lq = case
+    w = make_workload(name="mixed", kind="prefill", dtype="bf16", num_q_heads=HQ,
+                      num_kv_heads=HKV, head_dim=D, block_size=bs, seq_lens_k=lk, new_lens=lq,
+                      seed=sum(lk) % 991)
+    announce(f"mixed {case}")
+    dw = _mixed_run(w)
+    assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(True), "bf16", str(case))
+
+
+def test_mixed_all_prefill_equals_prefill_kernel():
+    """With no decode rows the mixed launch runs the prefill body: the same bits."""
+    w = config(4)
+    announce("mixed == prefill on the chunked-prefill workload")
+    dw = _mixed_run(w)
+    got = harness.from_device(dw.out).copy()
+    dw.attention()
+    torch.cuda.synchronize()
+    assert np.array_equal(got, harness.from_device(dw.out))
+
+
+def test_mixed_all_decode_equals_decode_kernel():
+    """With only decode rows the mixed launch runs the balanced decode body: the same bits."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 3000, size=40, endpoint=True).astype(np.int32)
+    w = make_workload(name="alldec", kind="prefill", dtype="bf16", num_q_heads=16, num_kv_heads=8,
+                      head_dim=128, block_size=256, seq_lens_k=lens, new_lens=np.ones(40, np.int32),
+                      seed=6)
+    announce("mixed == decode on 40 decode rows")
+    dw = _mixed_run(w)
+    assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(True), "bf16", "all decode")
+    out2 = torch.empty_like(dw.out)
+    nbytes = pk.pa_decode_workspace_size(40, 16, 8, 128, int(lens.max()), 0)
+    ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+    pk.pa_decode(out2, dw.q, dw.k_cache, dw.v_cache, dw.block_table, dw.seq_lens_k, w.scale,
+                 max_context_len=int(lens.max()), partition_size=0, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(harness.from_device(dw.out), harness.from_device(out2))
+
+
+def test_mixed_serving_step_workload():
+    """The benchmark's mixed step recipe (8 chunks of 256 over 1024 cached tokens plus
+    decode rows), with 64 of its 256 decode rows so the oracle stays quick."""
+    from workloads import make_mixed
+    w = make_mixed(num_decode=64)
+    announce(f"mixed serving step {w.name}")
+    dw = _mixed_run(w)
+    assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(True), "bf16", w.name)

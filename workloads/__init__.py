@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     Workload,
     bf16_bits_from_f32,
     make_config,
+    make_mixed,
     make_workload,
     nan_bits,
 )

@@ -254,6 +254,22 @@ def _c4(seed):
 CONFIGS = {0: _c0, 1: _c1, 2: _c2, 3: _c3, 4: _c4}
 
 
+def make_mixed(seed: int = 67005, num_decode: int = 256, num_prefill: int = 8) -> Workload:
+    """A serving step that mixes both kinds of rows (Qwen3-0.6B heads, block 256):
+    ``num_decode`` decode rows (one query each, contexts uniform in [128, 4096]) followed
+    by ``num_prefill`` chunks of 256 new tokens over 1024 cached ones."""
+    rng = np.random.default_rng(seed)
+    dec = rng.integers(128, 4096, size=num_decode, endpoint=True).astype(np.int32)
+    lens = np.concatenate([dec, np.full(num_prefill, 1024 + 256, dtype=np.int32)])
+    new = np.concatenate([np.ones(num_decode, dtype=np.int32),
+                          np.full(num_prefill, 256, dtype=np.int32)])
+    return make_workload(
+        name=f"qwen3-0.6b-mixed-{num_decode}dec-{num_prefill}x1280", kind="prefill",
+        dtype="bf16", num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+        seq_lens_k=lens, new_lens=new, pool_factor=1.25, max_blocks_per_seq=16,
+        scale=1.0 / math.sqrt(128), seed=seed, rng=rng)
+
+
 def make_config(index: int, seed: int | None = None) -> Workload:
     """Workload ``index`` (0-4) with its default seed ``67000 + index``."""
     if seed is None:
