@@ -8,8 +8,10 @@ tokens, the K/V scatter, the split-K decode pass and the log-sum-exp merge.
 Inputs are resident in HBM before the timed region.  The JSON line reports
 the whole step's algorithmic bytes per second as `value`, the decode pass's
 own HBM roofline, and the CPU oracle timed on a bounded sample of the same
-batch (whose outputs are also compared with the GPU's).  The chunked-prefill
-workload (8 x (1024 cached + 256 new) tokens) is timed as an extra.
+batch (whose outputs are also compared with the GPU's).  Extras: the
+chunked-prefill workload (8 x (1024 cached + 256 new) tokens), and a mixed
+serving step (256 decode rows + those 8 chunks) in one pa_attention_mixed
+launch against separate decode and prefill launches.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 """
@@ -182,6 +184,85 @@ def time_prefill(args):
             "timing": "HIP graph of one launch per buffer set, replayed between two events"}
 
 
+def _graph_us(fn, reps, rounds=5):
+    """Per-call GPU time of fn() (a few launches on the current stream), by HIP graph replay."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return float(np.median(per))
+
+
+def time_mixed(args):
+    """A mixed serving step: 256 decode rows + 8 chunks of 256 new tokens over 1024 cached,
+    one pa_attention_mixed call against separate pa_decode + pa_prefill_paged calls on the
+    same pool (both captured in HIP graphs and replayed)."""
+    import torch
+
+    import paged_kv_cache_67_amd as pk
+    from paged_kv_cache_67_amd import harness
+    from workloads import make_mixed
+
+    log("mixed: generating 256 decode rows + 8 x (1024 cached + 256 new)")
+    w = make_mixed()
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    dw.slot_mapping()
+    dw.store()
+    torch.cuda.synchronize()
+    dec = np.flatnonzero(w.new_lens == 1)
+    nd = len(dec)
+    assert np.array_equal(dec, np.arange(nd)), "decode rows lead the batch"
+    q_d, q_p = dw.q[:nd], dw.q[nd:]
+    out_d, out_p = torch.empty_like(q_d), torch.empty_like(q_p)
+    bt_d, bt_p = dw.block_table[:nd], dw.block_table[nd:]
+    ctx_d = dw.seq_lens_k[:nd]
+    cu_q_p = (dw.cu_q[nd:] - dw.cu_q[nd]).contiguous()
+    cu_k_p = (dw.cu_k[nd:] - dw.cu_k[nd]).contiguous()
+    max_ctx_d = int(w.seq_lens_k[:nd].max())
+    nbytes = pk.pa_decode_workspace_size(nd, w.num_q_heads, w.num_kv_heads, w.head_dim, max_ctx_d, 0)
+    ws_d = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+    max_q_p, max_k_p = int(w.new_lens[nd:].max()), int(w.seq_lens_k[nd:].max())
+
+    def separate():
+        pk.pa_decode(out_d, q_d, dw.k_cache, dw.v_cache, bt_d, ctx_d, w.scale,
+                     max_context_len=max_ctx_d, partition_size=0, workspace=ws_d)
+        pk.pa_prefill_paged(out_p, q_p, dw.k_cache, dw.v_cache, bt_p, cu_q_p, cu_k_p, max_q_p,
+                            max_k_p, w.scale, causal=True)
+
+    reps = max(20, args.steps // 5)
+    us_mixed = _graph_us(dw.attention_mixed, reps)
+    us_sep = _graph_us(separate, reps)
+    us_dec = _graph_us(lambda: pk.pa_decode(out_d, q_d, dw.k_cache, dw.v_cache, bt_d, ctx_d,
+                                            w.scale, max_context_len=max_ctx_d, partition_size=0,
+                                            workspace=ws_d), reps)
+    us_pf = _graph_us(lambda: pk.pa_prefill_paged(out_p, q_p, dw.k_cache, dw.v_cache, bt_p,
+                                                   cu_q_p, cu_k_p, max_q_p, max_k_p, w.scale,
+                                                   causal=True), reps)
+    same = bool(torch.equal(dw.out[:nd], out_d) and torch.equal(dw.out[nd:], out_p))
+    log(f"mixed step {us_mixed:.1f} us in one launch (+ merge); separate decode + prefill "
+        f"{us_sep:.1f} us (decode {us_dec:.1f}, prefill {us_pf:.1f}); outputs identical: {same}")
+    return {"workload": w.name, "decode_rows": nd, "prefill_chunks": int(w.num_seqs - nd),
+            "us_mixed_launch": round(us_mixed, 2), "us_separate_launches": round(us_sep, 2),
+            "us_decode_alone": round(us_dec, 2), "us_prefill_alone": round(us_pf, 2),
+            "outputs_identical": same,
+            "timing": "HIP graph of the call(s), replayed between two events"}
+
+
 def cpu_baseline(w, dw, seconds):
     """Time the CPU oracle on a bounded sample of the same batch; check the GPU on it too."""
     import oracle
@@ -267,6 +348,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with 3 x 1 GiB device copies (counter calibration runs)")
     ap.add_argument("--partition", type=int, default=0,
@@ -338,10 +420,16 @@ def main():
             result["note"] = "parity failed on the oracle sample: no time reported"
     else:
         result["cpu_baseline"] = None
+    del dw
+    torch.cuda.empty_cache()
+    extra = {}
     if not args.no_prefill:
-        del dw
+        extra["prefill"] = time_prefill(args)
         torch.cuda.empty_cache()
-        result["extra"] = {"prefill": time_prefill(args)}
+    if not args.no_mixed:
+        extra["mixed"] = time_mixed(args)
+    if extra:
+        result["extra"] = extra
     if args.copy_calibration:
         copy_calibration()
     print(json.dumps(result), flush=True)

@@ -9,13 +9,15 @@
 // 5), so one batch can hold prompt chunks and decode rows with no per-batch
 // prefill/decode switch.
 //
-// MI355X design.  One grid of 512-thread workgroups: the first n_pf run the
-// prefill body (query tiles of the sequences with Lq > 1, MFMA), the rest run
-// the balanced split-K decode body over the sequences with Lq = 1 (each wave
-// one (slice, KV-head tile) of the flattened decode keys).  Workgroups are
-// handed out in launch order, so decode slices fill the compute units as the
-// prefill tiles drain.  Decode rows cut by slice boundaries leave partial
-// states in the workspace; a second small launch merges them.
+// MI355X design.  One grid of 512-thread workgroups: the first n_pf (at most
+// one per compute unit) walk the list of query tiles of the sequences with
+// Lq > 1 (MFMA prefill body), the rest run the balanced split-K decode body over
+// the sequences with Lq = 1 (each wave one (slice, KV-head tile) of the
+// flattened decode keys).  Workgroups are handed out in launch order, so decode
+// slices fill the compute units as the prefill tiles drain; no workgroup is
+// launched for a decode row's would-be prefill tile.  Decode rows cut by slice
+// boundaries leave partial states in the workspace; a second small launch
+// merges them.
 #include "pa_decode_plan.h"
 #include "pa_prefill_dev.h"
 
@@ -28,13 +30,55 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_table, int maxb,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int total_q, int B,
-    int num_blocks, int bs_log2, int HQ, int HKV, float scale_log2, int n_pf, int nx,
+    int num_blocks, int bs_log2, int HQ, int HKV, float scale_log2, int n_pf,
     float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
     int32_t* __restrict__ ws_cuc, int head_waves, int Wt) {
   if ((int)blockIdx.x < n_pf) {
-    prefill_body<D, G, WIDE, true>(blockIdx.x, n_pf, nx, HKV, out, q, kc, vc, block_table, maxb,
-                                   cu_q, cu_k, total_q, num_blocks, bs_log2, HQ, HKV, scale_log2,
-                                   1);
+    // Prefill workgroups walk a list of the batch's query tiles, built here from cu_q: a
+    // sequence with Lq >= 2 has ceil(Lq / BM) tiles per KV head.  Items are numbered
+    // sequence, then KV head, then tile, and handed out so that consecutive items run on
+    // one XCD (tiles of one sequence and KV head read the same K/V rows through its L2).
+    constexpr int BM = kPrefillRows / G;
+    extern __shared__ int s_items[];  // [B + 1] exclusive prefix sums of tiles per sequence
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const int seg = (B + 63) / 64;
+      const int lo = min(B, lane * seg), hi = min(B, lo + seg);
+      int sum = 0;
+      for (int i = lo; i < hi; ++i) {
+        const int Lq = cu_q[i + 1] - cu_q[i];
+        sum += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      int run = incl - sum;
+      for (int i = lo; i < hi; ++i) {
+        s_items[i] = run;
+        const int Lq = cu_q[i + 1] - cu_q[i];
+        run += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
+      }
+      if (lane == 63) s_items[B] = incl;
+    }
+    __syncthreads();
+    const int items = HKV * lds_uniform(s_items + B);
+    for (int j = xcd_local_id(blockIdx.x, n_pf); j < items; j += n_pf) {
+      int lo = 0, hi = B;  // the sequence: largest b with HKV * s_items[b] <= j
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (HKV * lds_uniform(s_items + mid) <= j) lo = mid;
+        else hi = mid;
+      }
+      const int first = lds_uniform(s_items + lo);
+      const int T = lds_uniform(s_items + lo + 1) - first;
+      const int r = j - HKV * first;
+      prefill_body<D, G, WIDE, true>(r % T, r / T, lo, out, q, kc, vc, block_table, maxb, cu_q,
+                                     cu_k, total_q, num_blocks, bs_log2, HQ, HKV, scale_log2, 1);
+      __syncthreads();  // the next item reuses this item's LDS
+    }
   } else {
     const int i = blockIdx.x - n_pf;
     const int item = i * (kPrefillThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -47,7 +91,7 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
 
 typedef void (*mixed_fn)(uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                          const int32_t*, int, const int32_t*, const int32_t*, int, int, int, int,
-                         int, int, float, int, int, float*, float*, float*, int32_t*, int, int);
+                         int, int, float, int, float*, float*, float*, int32_t*, int, int);
 
 template <int D, bool WIDE>
 static mixed_fn pick_mixed_g(int G) {
@@ -129,9 +173,19 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   const bool wide = block_size >= kPrefillKeys;
   mixed_fn kern = head_dim == 64 ? (wide ? pick_mixed_g<64, true>(G) : pick_mixed_g<64, false>(G))
                                  : (wide ? pick_mixed_g<128, true>(G) : pick_mixed_g<128, false>(G));
+  // Prefill workgroups: at most one per compute unit, each looping over the tile list;
+  // fewer when the batch cannot hold that many tiles (sum over prefill sequences of
+  // ceil(Lq / BM) <= total_q / BM + number of such sequences).
   const int BM = kPrefillRows / G;
-  const int nx = max_seqlen_q > 1 ? (max_seqlen_q + BM - 1) / BM : 0;
-  const int64_t n_pf = (int64_t)nx * num_kv_heads * num_seqs;
+  int64_t n_pf = 0;
+  if (max_seqlen_q > 1) {
+    const int64_t seqs = num_seqs < total_q / 2 ? num_seqs : total_q / 2;
+    int64_t tiles = total_q / BM + seqs;
+    const int64_t by_len = (int64_t)num_seqs * ((max_seqlen_q + BM - 1) / BM);
+    tiles = tiles < by_len ? tiles : by_len;
+    n_pf = tiles * num_kv_heads;
+    n_pf = n_pf < kNumCUs ? n_pf : kNumCUs;
+  }
   const int head_waves = num_kv_heads * (G / head_tile(G));
   const int64_t n_dec = ceil_div((int64_t)pl.Wt * head_waves, kPrefillThreads / 64);
   if (n_pf + n_dec > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: grid too large", fn);
@@ -142,7 +196,7 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
                      (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, block_table, max_blocks_per_seq, cu_seqlens_q,
                      cu_seqlens_k, total_q, num_seqs, num_blocks, __builtin_ctz(block_size),
-                     num_q_heads, num_kv_heads, scale * kLog2e, (int)n_pf, nx, w.acc, w.m, w.l,
+                     num_q_heads, num_kv_heads, scale * kLog2e, (int)n_pf, w.acc, w.m, w.l,
                      w.cuc, head_waves, pl.Wt);
   int st = check_launch(fn);
   if (st) return st;

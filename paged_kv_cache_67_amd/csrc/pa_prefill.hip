@@ -35,10 +35,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_table, int maxb,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int total_q,
     int num_blocks, int bs_log2, int HQ, int HKV, float scale_log2, int causal) {
-  prefill_body<D, G, WIDE, false>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                                  gridDim.x * gridDim.y * gridDim.z, gridDim.x, gridDim.y, out, q,
-                                  kc, vc, block_table, maxb, cu_q, cu_k, total_q, num_blocks,
-                                  bs_log2, HQ, HKV, scale_log2, causal);
+  // Consecutive logical ids (query tiles of one sequence and KV head) share an XCD, so the
+  // tiles that read the same K/V rows hit the same L2.
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int lid = xcd_local_id(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
+  prefill_body<D, G, WIDE, false>(lid % nx, (lid / nx) % ny, lid / (nx * ny), out, q, kc, vc,
+                                  block_table, maxb, cu_q, cu_k, total_q, num_blocks, bs_log2, HQ,
+                                  HKV, scale_log2, causal);
 }
 
 typedef void (*prefill_fn)(uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,

@@ -54,13 +54,12 @@ __device__ __forceinline__ float max_over_groups(float x) {
 // odd) holds K_{t+2} and V_{t+1}, is written to LDS, and is refilled with K_{t+4} and
 // V_{t+3}.  WIDE (block_size >= 64): every tile lies inside one block, so a tile's address
 // is a scalar base plus a per-lane offset that does not change from tile to tile.
-// The body of one workgroup: launch index lin of nlin prefill workgroups over a
-// grid of nx query tiles x ny KV heads x sequences.  MIXED: the batch also holds
-// decode rows (sequences with one query), which the decode side of the launch
-// handles; such a sequence is skipped here.
+// The body of one workgroup item: query tile qt of sequence b for KV head g.  MIXED: the
+// batch also holds decode rows (sequences with one query), which the decode side of the
+// launch handles; such a sequence is skipped here.
 template <int D, int G, bool WIDE, bool MIXED>
 __device__ __forceinline__ void prefill_body(
-    int lin, int nlin, int nx, int ny, uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    int qt, int g, int b, uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int total_q, int num_blocks, int bs_log2, int HQ, int HKV,
@@ -81,10 +80,6 @@ __device__ __forceinline__ void prefill_body(
   static_assert(kBtCache % NT == 0, "block-table window split over the threads");
   __shared__ int s_bad;
 
-  // Consecutive logical ids (query tiles of one sequence and KV head) share an XCD, so the
-  // tiles that read the same K/V rows hit the same L2.
-  const int lid = xcd_local_id(lin, nlin);
-  const int qt = lid % nx, g = (lid / nx) % ny, b = lid / (nx * ny);
   const int tid = threadIdx.x;
   const int32_t* bt = block_table + (int64_t)b * maxb;
   // The first kBtCache block-table entries are fetched before the sequence lengths arrive
