@@ -11,7 +11,8 @@ own HBM roofline, and the CPU oracle timed on a bounded sample of the same
 batch (whose outputs are also compared with the GPU's).  Extras: the
 chunked-prefill workload (8 x (1024 cached + 256 new) tokens), and a mixed
 serving step (256 decode rows + those 8 chunks) in one pa_attention_mixed
-launch against separate decode and prefill launches.
+launch against separate decode and prefill launches, and decode steps of
+several batch sizes replayed from HIP graphs against eager launches.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 """
@@ -207,6 +208,64 @@ def _graph_us(fn, reps, rounds=5):
     return float(np.median(per))
 
 
+def time_graphs(w, dw, args):
+    """Decode steps (slot addressing + scatter + decode + merge) for the first n sequences
+    of the decode batch: launched eagerly from Python against replayed from the HIP graph
+    of their batch bucket (inputs copied into the graph's fixed buffers each step)."""
+    import torch
+
+    import paged_kv_cache_67_amd as pk
+    from paged_kv_cache_67_amd.graphs import GraphedDecode
+
+    runner = GraphedDecode(dw.k_cache, dw.v_cache, w.num_q_heads, w.block_table.shape[1],
+                           w.max_seqlen_k, w.scale, max_batch=w.num_seqs)
+    steps = max(50, args.steps)
+    res = {}
+    for n in (1, 8, 64, w.num_seqs):
+        q, kn, vn = dw.q[:n], dw.k_new[:n], dw.v_new[:n]
+        bt, ctx = dw.block_table[:n], dw.seq_lens_k[:n]
+        slots = torch.empty(n, dtype=torch.int32, device="cuda")
+        cu = torch.arange(n + 1, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q)
+        nbytes = pk.pa_decode_workspace_size(n, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                             w.max_seqlen_k, 0)
+        ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+
+        def eager():
+            pk.pa_slot_mapping(slots, bt, cu, ctx, w.block_size, w.num_blocks)
+            pk.pa_store_kv(kn, vn, dw.k_cache, dw.v_cache, slots)
+            pk.pa_decode(out, q, dw.k_cache, dw.v_cache, bt, ctx, w.scale,
+                         max_context_len=w.max_seqlen_k, partition_size=0, workspace=ws)
+
+        def graphed():
+            runner.step(q, kn, vn, bt, ctx)
+
+        graphed()  # captures the bucket and leaves these inputs in its buffers
+        replay = runner.graphs[runner.bucket(n)].replay
+
+        timing = {}
+        for name, fn in (("eager", eager), ("graph", graphed), ("replay", replay)):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            timing[name] = e0.elapsed_time(e1) * 1e3 / steps
+        same = bool(torch.equal(out, runner.out[:n]))
+        res[str(n)] = {"bucket": runner.bucket(n), "us_eager": round(timing["eager"], 2),
+                       "us_graph_with_input_copies": round(timing["graph"], 2),
+                       "us_graph_replay": round(timing["replay"], 2), "outputs_identical": same}
+        log(f"graphs: batch {n}: eager {timing['eager']:.1f} us/step; graph (bucket "
+            f"{runner.bucket(n)}) {timing['replay']:.1f} us/step with the inputs in its buffers, "
+            f"{timing['graph']:.1f} with six torch copies in; identical {same}")
+    return {"workload": w.name, "steps": steps, "by_batch": res,
+            "timing": "events around back-to-back steps launched from Python"}
+
+
 def time_mixed(args):
     """A mixed serving step: 256 decode rows + 8 chunks of 256 new tokens over 1024 cached,
     one pa_attention_mixed call against separate pa_decode + pa_prefill_paged calls on the
@@ -349,6 +408,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with 3 x 1 GiB device copies (counter calibration runs)")
     ap.add_argument("--partition", type=int, default=0,
@@ -420,9 +480,11 @@ def main():
             result["note"] = "parity failed on the oracle sample: no time reported"
     else:
         result["cpu_baseline"] = None
+    extra = {}
+    if not args.no_graphs:
+        extra["graphs"] = time_graphs(w, dw, args)
     del dw
     torch.cuda.empty_cache()
-    extra = {}
     if not args.no_prefill:
         extra["prefill"] = time_prefill(args)
         torch.cuda.empty_cache()

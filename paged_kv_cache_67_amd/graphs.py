@@ -1,0 +1,128 @@
+"""Decode steps replayed from HIP graphs, one per batch-size bucket.
+
+A serving loop runs the same decode step over and over with a batch size that
+changes from step to step.  The nano-vLLM lab manual (B.4 and Fig. B-6)
+captures the decode step once per batch-size bucket (1, 2, 4, 8, 16, then
+steps of 16), copies each step's inputs into the captured fixed buffers and
+replays: a batch of 9 replays the 16-row graph, and the 7 padded rows have
+slot -1 and context length 0, so they write no cache row.  B.5 adds that a
+batch no bucket covers runs eagerly instead of failing.  Both hold here for the
+library's kernels: slot addressing gives -1 for a row with context 0 (the
+scatter skips it), decode gives such a row zeros without reading the cache,
+and the library allocates nothing and never synchronises, so the captured
+launches are the eager ones.
+
+    runner = GraphedDecode(k_cache, v_cache, num_q_heads=16, max_blocks_per_seq=16,
+                           max_context_len=4096, scale=1 / 128 ** 0.5, max_batch=256)
+    out = runner.step(q, k_new, v_new, block_table, context_lens)
+"""
+
+from __future__ import annotations
+
+import bisect
+
+import torch
+
+from . import _binding as pa
+
+
+def default_buckets(max_batch):
+    """1, 2, 4, 8, 16, then multiples of 16 up to max_batch (which is always a bucket)."""
+    out = [b for b in (1, 2, 4, 8, 16) if b < max_batch]
+    out += list(range(32, max_batch, 16))
+    return tuple(out + [int(max_batch)])
+
+
+class GraphedDecode:
+    """slot addressing + K/V scatter + decode for one layer, replayed per batch bucket.
+
+    Buffers are sized for the largest bucket.  ``step`` copies the live rows in,
+    marks the rows up to the bucket as padding (context 0) and replays that
+    bucket's graph (capturing it on first use).  The K/V pools are the caller's
+    and are updated in place.
+    """
+
+    def __init__(self, k_cache, v_cache, num_q_heads, max_blocks_per_seq, max_context_len, scale,
+                 max_batch=256, buckets=None):
+        NB, BS, HKV, D = k_cache.shape
+        assert v_cache.shape == k_cache.shape and k_cache.is_cuda
+        self.k_cache, self.v_cache = k_cache, v_cache
+        if buckets is None:
+            buckets = default_buckets(max_batch)
+        self.buckets = tuple(sorted(set(int(b) for b in buckets)))
+        self.max_context_len = int(max_context_len)
+        self.scale = float(scale)
+        self.block_size, self.num_blocks = BS, NB
+        bmax = self.buckets[-1]
+        dev, dt = k_cache.device, k_cache.dtype
+        self.q = torch.zeros(bmax, num_q_heads, D, dtype=dt, device=dev)
+        self.k_new = torch.zeros(bmax, HKV, D, dtype=dt, device=dev)
+        self.v_new = torch.zeros(bmax, HKV, D, dtype=dt, device=dev)
+        self.out = torch.zeros(bmax, num_q_heads, D, dtype=dt, device=dev)
+        self.block_table = torch.full((bmax, max_blocks_per_seq), -1, dtype=torch.int32, device=dev)
+        self.context_lens = torch.zeros(bmax, dtype=torch.int32, device=dev)
+        self.cu_q = torch.arange(bmax + 1, dtype=torch.int32, device=dev)
+        self.slots = torch.full((bmax,), -1, dtype=torch.int32, device=dev)
+        nbytes = pa.pa_decode_workspace_size(bmax, num_q_heads, HKV, D, self.max_context_len, 0)
+        self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=dev)
+        self.graphs = {}
+
+    def bucket(self, batch):
+        """The smallest bucket that holds `batch` rows, or None if none does."""
+        i = bisect.bisect_left(self.buckets, batch)
+        return self.buckets[i] if i < len(self.buckets) else None
+
+    def _launch(self, b):
+        pa.pa_slot_mapping(self.slots[:b], self.block_table[:b], self.cu_q[:b + 1],
+                           self.context_lens[:b], self.block_size, self.num_blocks)
+        pa.pa_store_kv(self.k_new[:b], self.v_new[:b], self.k_cache, self.v_cache, self.slots[:b])
+        pa.pa_decode(self.out[:b], self.q[:b], self.k_cache, self.v_cache, self.block_table[:b],
+                     self.context_lens[:b], self.scale, max_context_len=self.max_context_len,
+                     partition_size=0, workspace=self.workspace)
+
+    def capture(self, b):
+        """Capture bucket b (the buffers' current rows are run once eagerly first)."""
+        if b not in self.graphs:
+            self._launch(b)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._launch(b)
+            self.graphs[b] = g
+        return self.graphs[b]
+
+    def eager(self, q, k_new, v_new, block_table, context_lens):
+        """The same step launched directly on the caller's tensors (no graph)."""
+        n = q.shape[0]
+        dev = q.device
+        slots = torch.empty(n, dtype=torch.int32, device=dev)
+        cu_q = torch.arange(n + 1, dtype=torch.int32, device=dev)
+        pa.pa_slot_mapping(slots, block_table, cu_q, context_lens, self.block_size, self.num_blocks)
+        pa.pa_store_kv(k_new, v_new, self.k_cache, self.v_cache, slots)
+        out = torch.empty_like(q)
+        nbytes = pa.pa_decode_workspace_size(n, q.shape[1], self.k_cache.shape[2], q.shape[2],
+                                             self.max_context_len, 0)
+        ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=dev)
+        pa.pa_decode(out, q, self.k_cache, self.v_cache, block_table, context_lens, self.scale,
+                     max_context_len=self.max_context_len, partition_size=0, workspace=ws)
+        return out
+
+    def step(self, q, k_new, v_new, block_table, context_lens):
+        """One decode step for the live rows; returns a view of the output rows (a new
+        tensor when the batch is larger than every bucket and runs eagerly)."""
+        n = q.shape[0]
+        b = self.bucket(n)
+        if b is None:
+            return self.eager(q, k_new, v_new, block_table, context_lens)
+        self.q[:n].copy_(q)
+        self.k_new[:n].copy_(k_new)
+        self.v_new[:n].copy_(v_new)
+        w = block_table.shape[1]
+        self.block_table[:n, :w].copy_(block_table)
+        if w < self.block_table.shape[1]:
+            self.block_table[:n, w:].fill_(-1)
+        self.context_lens[:n].copy_(context_lens)
+        self.context_lens[n:b].zero_()  # padding rows: no keys, no cache write
+        g = self.capture(b)
+        g.replay()
+        return self.out[:n]
