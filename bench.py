@@ -152,37 +152,33 @@ def time_prefill(args):
         dw.store()
         sets.append(dw)
     torch.cuda.synchronize()
-    for dw in sets:  # warm-up outside the graph
-        dw.attention()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for dw in sets:
-            dw.attention()
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = max(10, args.steps // 5)
-    per = []
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        per.append(e0.elapsed_time(e1) * 1e3 / (reps * len(sets)))
     L, lq = int(w.seq_lens_k[0]), int(w.new_lens[0])
     pairs = sum(L - lq + i + 1 for i in range(lq))  # causal-masked (query, key) pairs per head
     flops = 4.0 * w.head_dim * pairs * w.num_q_heads * w.num_seqs
-    us = float(np.median(per))
+    reps = max(10, args.steps // 5)
+
+    def all_sets():
+        for dw in sets:
+            dw.attention()
+
+    us = _graph_us(all_sets, reps) / len(sets)
     tf = flops / (us * 1e-6) / 1e12
     log(f"prefill {us:.1f} us per launch (graph replay), {tf:.1f} TFLOP/s")
-    return {"workload": w.name, "kernel": "pa_prefill_paged", "us_per_launch": round(us, 2),
-            "launches_timed": 5 * reps * len(sets), "gflop": round(flops / 1e9, 3),
-            "tflops": round(tf, 1), "peak_tflops": BF16_PEAK_TFLOPS,
-            "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4), "buffer_sets": len(sets),
-            "timing": "HIP graph of one launch per buffer set, replayed between two events"}
+    res = {"workload": w.name, "kernel": "pa_prefill_paged", "us_per_launch": round(us, 2),
+           "launches_timed": 5 * reps * len(sets), "gflop": round(flops / 1e9, 3),
+           "tflops": round(tf, 1), "peak_tflops": BF16_PEAK_TFLOPS,
+           "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4), "buffer_sets": len(sets),
+           "timing": "HIP graph of one launch per buffer set, replayed between two events"}
+    for dw in sets:  # the same inputs stored as fp16
+        dw.k_cache, dw.v_cache = dw.k_cache.to(torch.float16), dw.v_cache.to(torch.float16)
+        dw.q, dw.out = dw.q.to(torch.float16), dw.out.to(torch.float16)
+    torch.cuda.synchronize()
+    us16 = _graph_us(all_sets, reps) / len(sets)
+    tf16 = flops / (us16 * 1e-6) / 1e12
+    log(f"prefill fp16 {us16:.1f} us per launch, {tf16:.1f} TFLOP/s")
+    res["f16"] = {"us_per_launch": round(us16, 2), "tflops": round(tf16, 1),
+                  "frac_of_peak": round(tf16 / BF16_PEAK_TFLOPS, 4)}
+    return res
 
 
 def _graph_us(fn, reps, rounds=5):
@@ -264,6 +260,33 @@ def time_graphs(w, dw, args):
             f"{timing['graph']:.1f} with six torch copies in; identical {same}")
     return {"workload": w.name, "steps": steps, "by_batch": res,
             "timing": "events around back-to-back steps launched from Python"}
+
+
+def time_f16_decode(w, dw, args):
+    """pa_decode (both passes) on the decode batch with bf16 storage and with the same
+    inputs converted to fp16 on the device (same shapes and bytes), by HIP graph replay."""
+    import torch
+
+    import paged_kv_cache_67_amd as pk
+
+    nbytes = pk.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         w.max_seqlen_k, 0)
+    ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+    kv, q, bt = decode_bytes(w)
+    res = {}
+    reps = max(20, args.steps // 5)
+    for name, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        kc, vc, qq = dw.k_cache.to(tdt), dw.v_cache.to(tdt), dw.q.to(tdt)
+        out = torch.empty_like(qq)
+        us = _graph_us(lambda: pk.pa_decode(out, qq, kc, vc, dw.block_table, dw.seq_lens_k, w.scale,
+                                            max_context_len=w.max_seqlen_k, partition_size=0,
+                                            workspace=ws), reps)
+        gbs = (kv + 2 * q + bt) / (us * 1e-6) / 1e9
+        res[name] = {"us_pa_decode": round(us, 2), "GBps": round(gbs, 1)}
+        log(f"pa_decode {name}: {us:.1f} us, {gbs:.1f} GB/s (both passes, graph replay)")
+        del kc, vc, qq, out
+        torch.cuda.empty_cache()
+    return {"workload": w.name, **res}
 
 
 def time_mixed(args):
@@ -409,6 +432,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-graphs", action="store_true")
+    ap.add_argument("--no-f16", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with 3 x 1 GiB device copies (counter calibration runs)")
     ap.add_argument("--partition", type=int, default=0,
@@ -481,6 +505,8 @@ def main():
     else:
         result["cpu_baseline"] = None
     extra = {}
+    if not args.no_f16:
+        extra["f16_decode"] = time_f16_decode(w, dw, args)
     if not args.no_graphs:
         extra["graphs"] = time_graphs(w, dw, args)
     del dw

@@ -30,12 +30,14 @@
  *   at row t % block_size ([MinivLLM], paged_attention_decode_kernel).
  * - block_table is int32 [num_seqs][max_blocks_per_seq], row-major, padded
  *   with -1 past each sequence's last block ([MinivLLM], prepare_decode).
- * - Element types: PA_F32 (float) or PA_BF16 (bfloat16 bits); q, out, key,
- *   value and both caches share one type.  head_dim is 64 or 128.
+ * - Element types: PA_F32 (float), PA_BF16 (bfloat16 bits) or PA_F16 (IEEE
+ *   half); q, out, key, value and both caches share one type.  head_dim is 64
+ *   or 128.
  *   block_size is a power of two in [8, 1024].
  * - Base pointers of q, out, key, value, caches and workspace must be 16-byte
  *   aligned.
- * - Arithmetic: fp32 accumulation; bf16 results are rounded to nearest-even.
+ * - Arithmetic: fp32 accumulation; bf16 and fp16 results are rounded to
+ *   nearest-even.
  * - Device-side contents (slot values, block ids, lengths) are the caller's
  *   contract and are not validated on the host: slot_mapping entries are -1
  *   or in [0, num_blocks*block_size) and distinct; block ids read for live
@@ -67,7 +69,7 @@ typedef enum pa_status {
   PA_ERR_HIP = 6          /* the HIP runtime rejected a launch */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 
 /* Library version as major*10000 + minor*100 + patch. */
 int pa_version(void);
@@ -249,7 +251,8 @@ int pa_decode_merge(void* out, const void* workspace, const int32_t* context_len
  *   cu_seqlens_k in   int32 [num_seqs + 1], Lk >= Lq for every sequence
  *   max_seqlen_q / max_seqlen_k   host upper bounds of Lq / Lk
  *
- * dtype must be PA_BF16 (the matrix-core path) and scale must be > 0.
+ * dtype must be PA_BF16 or PA_F16 (the matrix-core path) and scale must be
+ * > 0.
  */
 int pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -287,7 +290,7 @@ size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t nu
  *                num_kv_heads, head_dim, max_seqlen_k) bytes, 16-byte aligned,
  *                owned by the caller; no initialisation needed
  *
- * dtype must be PA_BF16, scale > 0, num_seqs <= 4096, num_q_heads/num_kv_heads
+ * dtype must be PA_BF16 or PA_F16, scale > 0, num_seqs <= 4096, num_q_heads/num_kv_heads
  * in 1..8 or 16.  Errors as for pa_prefill_paged, plus PA_ERR_WORKSPACE for a
  * missing or short workspace.
  */

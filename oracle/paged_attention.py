@@ -38,8 +38,8 @@ What each function is pinned by (tests/test_oracle_pins.py, tests/golden/):
                         Fig. B-5 and [mini] section 5); one partition is the
                         identity.  Pinned against ``decode``, which is pinned.
 
-Storage dtypes arrive as raw bits (``uint16`` for bfloat16, ``float32`` for
-fp32) and are widened exactly to float64 by ``to_f64``.
+Storage dtypes arrive as raw bits (``uint16`` for bfloat16, ``float16`` for
+fp16, ``float32`` for fp32) and are widened exactly to float64 by ``to_f64``.
 """
 
 from __future__ import annotations
@@ -54,6 +54,8 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
         return u.view(np.float32).astype(np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
     raise ValueError(dtype)
 
 

@@ -9,6 +9,7 @@ call does, and fails loudly if it has not been built.
 
 from ._binding import (  # noqa: F401
     PA_BF16,
+    PA_F16,
     PA_F32,
     PAError,
     lib,

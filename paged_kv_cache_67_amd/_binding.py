@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 _lib = None
 
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
           4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
 
@@ -87,6 +87,8 @@ def _dtype(t) -> int:
         return PA_BF16
     if t.dtype == torch.float32:
         return PA_F32
+    if t.dtype == torch.float16:
+        return PA_F16
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 

@@ -35,15 +35,15 @@ namespace pa {
 // (sequence, KV head, head tile, partition); the waves of a workgroup are
 // consecutive KV heads of the same tokens.  split == 0: one partition per
 // sequence, written straight to `out`.
-template <int D, bool BF16, int G>
+template <int D, int ET, int G>
 __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_kernel(
     void* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_m,
     float* __restrict__ ws_l, const void* __restrict__ qptr, const void* __restrict__ kcache,
     const void* __restrict__ vcache, const int32_t* __restrict__ block_table, int maxb,
     const int32_t* __restrict__ context_lens, int num_blocks, int bs_log2, int HQ, int HKV,
     int group, float scale_log2, int part_size, int NP, int split) {
-  using W = DecodeWave<D, BF16, G>;
-  using E = Elem<BF16>;
+  using W = DecodeWave<D, ET, G>;
+  using E = Elem<ET>;
   constexpr int CH = W::CH;
   constexpr int U = W::U;
 
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_kernel(
 }
 
 // Standalone balanced kernel: grid = (slice, head group), one head wave per wave.
-template <int D, bool BF16, int G>
+template <int D, int ET, int G>
 __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel(
     void* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_m,
     float* __restrict__ ws_l, int32_t* __restrict__ ws_cuc, const void* __restrict__ qptr,
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel
     const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ context_lens,
     int B, int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt) {
   const int hw = blockIdx.y * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  decode_balanced_body<D, BF16, G, false>(
+  decode_balanced_body<D, ET, G, false>(
       blockIdx.x, hw, blockIdx.x == 0 && blockIdx.y == 0, out, ws_acc, ws_m, ws_l, ws_cuc, qptr,
       kcache, vcache, block_table, maxb, context_lens, nullptr, nullptr, 0, B, num_blocks, bs_log2,
       HQ, HKV, group, scale_log2, Wt);
@@ -122,12 +122,12 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel
 // ---------------------------------------------------------------------------
 // Merges: one workgroup per (query head, sequence), one thread per element.
 
-template <bool BF16>
+template <int ET>
 __global__ __launch_bounds__(128) void merge_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const int32_t* __restrict__ context_lens, int HQ, int D,
     int NP, int part_size) {
-  using E = Elem<BF16>;
+  using E = Elem<ET>;
   const int h = blockIdx.x, b = blockIdx.y;
   const int64_t bh = (int64_t)b * HQ + h;
   const int L = context_lens[b];
@@ -160,13 +160,13 @@ typedef void (*balanced_fn)(void*, float*, float*, float*, int32_t*, const void*
                             const void*, const int32_t*, int, const int32_t*, int, int, int, int,
                             int, int, float, int);
 
-template <int D, bool BF16>
+template <int D, int ET>
 static void pick_g(int G, decode_fn* f, balanced_fn* fb) {
   switch (G) {
-#define PA_CASE(g)                            \
-  case g:                                     \
-    *f = decode_kernel<D, BF16, g>;           \
-    *fb = decode_balanced_kernel<D, BF16, g>; \
+#define PA_CASE(g)                          \
+  case g:                                   \
+    *f = decode_kernel<D, ET, g>;           \
+    *fb = decode_balanced_kernel<D, ET, g>; \
     return;
     PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
 #undef PA_CASE
@@ -176,8 +176,9 @@ static void pick_g(int G, decode_fn* f, balanced_fn* fb) {
 }
 
 static void pick_decode(int D, pa_dtype dt, int G, decode_fn* f, balanced_fn* fb) {
-  if (dt == PA_BF16) D == 64 ? pick_g<64, true>(G, f, fb) : pick_g<128, true>(G, f, fb);
-  else D == 64 ? pick_g<64, false>(G, f, fb) : pick_g<128, false>(G, f, fb);
+  if (dt == PA_BF16) D == 64 ? pick_g<64, PA_BF16>(G, f, fb) : pick_g<128, PA_BF16>(G, f, fb);
+  else if (dt == PA_F16) D == 64 ? pick_g<64, PA_F16>(G, f, fb) : pick_g<128, PA_F16>(G, f, fb);
+  else D == 64 ? pick_g<64, PA_F32>(G, f, fb) : pick_g<128, PA_F32>(G, f, fb);
 }
 
 static int validate_common(const char* fn, int32_t num_seqs, int32_t num_q_heads,
@@ -190,7 +191,8 @@ static int validate_common(const char* fn, int32_t num_seqs, int32_t num_q_heads
                 num_kv_heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
-  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
   return PA_OK;
 }
 
@@ -212,21 +214,21 @@ static int launch_merge(void* out, const DecodePlan& pl, const WsPtrs& w,
                         const int32_t* context_lens, int32_t B, int32_t HQ, int32_t D,
                         pa_dtype dtype, hipStream_t s) {
   dim3 grid(HQ, B), block(D <= 128 ? D : 128);
-  if (pl.mode == DecodePlan::kBalanced) {
-    if (dtype == PA_BF16)
-      hipLaunchKernelGGL((merge_balanced_kernel<true, false>), grid, block, 0, s, out, w.acc, w.m,
-                         w.l, w.cuc, nullptr, 0, B, HQ, D, pl.Wt);
-    else
-      hipLaunchKernelGGL((merge_balanced_kernel<false, false>), grid, block, 0, s, out, w.acc, w.m,
-                         w.l, w.cuc, nullptr, 0, B, HQ, D, pl.Wt);
+#define PA_MERGE(ET)                                                                          \
+  if (pl.mode == DecodePlan::kBalanced)                                                       \
+    hipLaunchKernelGGL((merge_balanced_kernel<ET, false>), grid, block, 0, s, out, w.acc, w.m, \
+                       w.l, w.cuc, nullptr, 0, B, HQ, D, pl.Wt);                              \
+  else                                                                                        \
+    hipLaunchKernelGGL(merge_kernel<ET>, grid, block, 0, s, out, w.acc, w.m, w.l,             \
+                       context_lens, HQ, D, pl.NP, pl.P);
+  if (dtype == PA_BF16) {
+    PA_MERGE(PA_BF16)
+  } else if (dtype == PA_F16) {
+    PA_MERGE(PA_F16)
   } else {
-    if (dtype == PA_BF16)
-      hipLaunchKernelGGL(merge_kernel<true>, grid, block, 0, s, out, w.acc, w.m, w.l, context_lens,
-                         HQ, D, pl.NP, pl.P);
-    else
-      hipLaunchKernelGGL(merge_kernel<false>, grid, block, 0, s, out, w.acc, w.m, w.l,
-                         context_lens, HQ, D, pl.NP, pl.P);
+    PA_MERGE(PA_F32)
   }
+#undef PA_MERGE
   return check_launch("decode merge");
 }
 

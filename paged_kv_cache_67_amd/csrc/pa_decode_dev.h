@@ -9,14 +9,16 @@ namespace pa {
 
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// Element handling per storage type.  A lane owns 16 bytes of a token row:
-// 8 bf16 or 4 fp32 values.  q.k uses v_dot2_f32_bf16 on the packed bf16 pairs
-// (products exact, fp32 accumulation); V is widened to fp32 for the P.V sums.
-template <bool BF16>
+// Element handling per storage type (ET = pa_dtype).  A lane owns 16 bytes of a
+// token row: 8 bf16 / fp16 or 4 fp32 values.  q.k uses v_dot2_f32_bf16 or
+// v_dot2_f32_f16 on the packed pairs (products exact, fp32 accumulation); V is
+// widened to fp32 for the P.V sums.
+template <int ET>
 struct Elem;
 template <>
-struct Elem<true> {
+struct Elem<PA_BF16> {
   static constexpr int VEC = 8;
   __device__ static float dot(const uint32_t* q, const uint4& k) {
     float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[0]),
@@ -38,7 +40,34 @@ struct Elem<true> {
   }
 };
 template <>
-struct Elem<false> {
+struct Elem<PA_F16> {
+  static constexpr int VEC = 8;
+  __device__ static float dot(const uint32_t* q, const uint4& k) {
+    float d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[0]),
+                                     __builtin_bit_cast(f16x2_t, k.x), 0.0f, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[1]), __builtin_bit_cast(f16x2_t, k.y),
+                               d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[2]), __builtin_bit_cast(f16x2_t, k.z),
+                               d, false);
+    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q[3]), __builtin_bit_cast(f16x2_t, k.w),
+                               d, false);
+    return d;
+  }
+  __device__ static void widen(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
+      f[2 * i] = (float)h[0];
+      f[2 * i + 1] = (float)h[1];
+    }
+  }
+  __device__ static void store(void* out, int64_t idx, float v) {
+    reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
+  }
+};
+template <>
+struct Elem<PA_F32> {
   static constexpr int VEC = 4;
   __device__ static float dot(const uint32_t* q, const uint4& k) {
     float d = __uint_as_float(q[0]) * __uint_as_float(k.x);
@@ -71,8 +100,8 @@ __host__ __device__ constexpr int loads_per_chunk(int G) {
 // up to 512 VGPRs).
 __host__ __device__ constexpr int max_head_waves(int G) { return G > 6 ? 4 : 8; }
 // Tokens per chunk for a kernel instance: rows per load times load slots.
-__host__ __device__ constexpr int chunk_tokens(int D, bool bf16, int G) {
-  return (64 / (D / (bf16 ? 8 : 4))) * loads_per_chunk(G);
+__host__ __device__ constexpr int chunk_tokens(int D, int elt_size, int G) {
+  return (64 / (D / (16 / elt_size))) * loads_per_chunk(G);
 }
 
 // Query heads per decode wave: the largest divisor of the GQA group that is <= 8.
@@ -93,15 +122,15 @@ struct KVRegs {
 
 // Per-wave decode state: this wave's q registers and one online-softmax state
 // per row group, for G query heads of one KV head.
-template <int D, bool BF16, int G>
+template <int D, int ET, int G>
 struct DecodeWave {
-  using E = Elem<BF16>;
+  using E = Elem<ET>;
   static constexpr int VEC = E::VEC;
   static constexpr int LANES = D / VEC;  // lanes per token row
   static constexpr int RG = 64 / LANES;  // token rows per wave load
   static constexpr int U = loads_per_chunk(G);
   static constexpr int CH = RG * U;  // tokens per chunk
-  static constexpr int ESZ = BF16 ? 2 : 4;
+  static constexpr int ESZ = ET == PA_F32 ? 4 : 2;
 
   int r, sl;  // row group, 16-byte slice of the row
   int bs_log2, bs_mask, maxb, num_blocks;
@@ -322,7 +351,7 @@ __device__ __forceinline__ Cursor cursor_next(Cursor c, int B, const int* s_cuc,
 // a sequence with exactly one query (a decode row, q row cu_q[b]) attends its
 // cu_k length of keys, any other sequence counts as empty here.  Otherwise
 // sequence b attends context_lens[b] keys with q / out row b.
-template <int D, bool BF16, int G, bool VARLEN>
+template <int D, int ET, int G, bool VARLEN>
 __device__ __forceinline__ void decode_balanced_body(
     int w, int hw, bool write_cuc, void* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_cuc,
@@ -331,7 +360,7 @@ __device__ __forceinline__ void decode_balanced_body(
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int total_q, int B, int num_blocks, int bs_log2, int HQ,
     int HKV, int group, float scale_log2, int Wt) {
-  using W = DecodeWave<D, BF16, G>;
+  using W = DecodeWave<D, ET, G>;
   constexpr int CH = W::CH;
   constexpr int U = W::U;
   extern __shared__ int s_mem[];
@@ -459,12 +488,12 @@ __device__ __forceinline__ void decode_balanced_body(
 // are slice w0's tail state and slices w0+1 .. w1's head states.  VARLEN: only
 // the one-query sequences of a varlen batch are decode rows (row cu_q[b]); the
 // others belong to the prefill side and are left alone.
-template <bool BF16, bool VARLEN>
+template <int ET, bool VARLEN>
 __global__ __launch_bounds__(128) void merge_balanced_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const int32_t* __restrict__ ws_cuc,
     const int32_t* __restrict__ cu_q, int total_q, int B, int HQ, int D, int Wt) {
-  using E = Elem<BF16>;
+  using E = Elem<ET>;
   const int h = blockIdx.x, b = blockIdx.y;
   int rb = b;
   if constexpr (VARLEN) {

@@ -39,7 +39,7 @@ inline DecodePlan plan_decode(int32_t B, int32_t HQ, int32_t HKV, int32_t D, pa_
   } else if (partition_size == 0 && B <= kMaxBalancedSeqs) {
     pl.mode = DecodePlan::kBalanced;
     const int head_waves = HKV * (group / pl.G);
-    const int CH = chunk_tokens(D, dtype == PA_BF16, pl.G);
+    const int CH = chunk_tokens(D, elt_bytes(dtype), pl.G);
     int64_t Wt = (int64_t)kNumCUs * PA_DECODE_WAVES_PER_CU / head_waves;
     Wt = Wt < 1 ? 1 : Wt;
     const int64_t max_chunks = (int64_t)B * ceil_div(max_ctx > 0 ? max_ctx : 1, CH);

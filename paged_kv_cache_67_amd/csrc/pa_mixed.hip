@@ -25,7 +25,7 @@ namespace pa {
 
 constexpr int kMaxMixedSeqs = 4096;  // LDS holds 3 ints per sequence beside the prefill tiles
 
-template <int D, int G, bool WIDE>
+template <int D, int G, bool WIDE, int ET>
 __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_table, int maxb,
@@ -75,14 +75,14 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
       const int first = lds_uniform(s_items + lo);
       const int T = lds_uniform(s_items + lo + 1) - first;
       const int r = j - HKV * first;
-      prefill_body<D, G, WIDE, true>(r % T, r / T, lo, out, q, kc, vc, block_table, maxb, cu_q,
+      prefill_body<D, G, WIDE, true, ET>(r % T, r / T, lo, out, q, kc, vc, block_table, maxb, cu_q,
                                      cu_k, total_q, num_blocks, bs_log2, HQ, HKV, scale_log2, 1);
       __syncthreads();  // the next item reuses this item's LDS
     }
   } else {
     const int i = blockIdx.x - n_pf;
     const int item = i * (kPrefillThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    decode_balanced_body<D, true, head_tile(G), true>(
+    decode_balanced_body<D, ET, head_tile(G), true>(
         item / head_waves, item % head_waves, i == 0, out, ws_acc, ws_m, ws_l, ws_cuc, q, kc, vc,
         block_table, maxb, nullptr, cu_q, cu_k, total_q, B, num_blocks, bs_log2, HQ, HKV, G,
         scale_log2, Wt);
@@ -93,20 +93,26 @@ typedef void (*mixed_fn)(uint16_t*, const uint16_t*, const uint16_t*, const uint
                          const int32_t*, int, const int32_t*, const int32_t*, int, int, int, int,
                          int, int, float, int, float*, float*, float*, int32_t*, int, int);
 
-template <int D, bool WIDE>
+template <int D, bool WIDE, int ET>
 static mixed_fn pick_mixed_g(int G) {
   switch (G) {
-    case 1: return mixed_kernel<D, 1, WIDE>;
-    case 2: return mixed_kernel<D, 2, WIDE>;
-    case 3: return mixed_kernel<D, 3, WIDE>;
-    case 4: return mixed_kernel<D, 4, WIDE>;
-    case 5: return mixed_kernel<D, 5, WIDE>;
-    case 6: return mixed_kernel<D, 6, WIDE>;
-    case 7: return mixed_kernel<D, 7, WIDE>;
-    case 8: return mixed_kernel<D, 8, WIDE>;
-    case 16: return mixed_kernel<D, 16, WIDE>;
+    case 1: return mixed_kernel<D, 1, WIDE, ET>;
+    case 2: return mixed_kernel<D, 2, WIDE, ET>;
+    case 3: return mixed_kernel<D, 3, WIDE, ET>;
+    case 4: return mixed_kernel<D, 4, WIDE, ET>;
+    case 5: return mixed_kernel<D, 5, WIDE, ET>;
+    case 6: return mixed_kernel<D, 6, WIDE, ET>;
+    case 7: return mixed_kernel<D, 7, WIDE, ET>;
+    case 8: return mixed_kernel<D, 8, WIDE, ET>;
+    case 16: return mixed_kernel<D, 16, WIDE, ET>;
   }
   return nullptr;
+}
+
+template <int ET>
+static mixed_fn pick_mixed(int D, bool wide, int G) {
+  if (D == 64) return wide ? pick_mixed_g<64, true, ET>(G) : pick_mixed_g<64, false, ET>(G);
+  return wide ? pick_mixed_g<128, true, ET>(G) : pick_mixed_g<128, false, ET>(G);
 }
 
 }  // namespace pa
@@ -139,7 +145,8 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   if (num_q_heads % num_kv_heads)
     return fail(PA_ERR_SHAPE, "%s: q_heads %d not a multiple of kv_heads %d", fn, num_q_heads,
                 num_kv_heads);
-  if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_BF16", fn);
+  if (dtype != PA_BF16 && dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype must be PA_BF16 or PA_F16", fn);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
   if (!is_pow2(block_size) || block_size < 8 || block_size > 1024)
@@ -164,15 +171,15 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (workspace && !aligned16(workspace)))
     return fail(PA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
-  const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, PA_BF16,
+  const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
                                     max_seqlen_k > 0 ? max_seqlen_k : 1, 0, true);
   if (!workspace || workspace_bytes < pl.ws_bytes)
     return fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
                 pl.ws_bytes);
 
   const bool wide = block_size >= kPrefillKeys;
-  mixed_fn kern = head_dim == 64 ? (wide ? pick_mixed_g<64, true>(G) : pick_mixed_g<64, false>(G))
-                                 : (wide ? pick_mixed_g<128, true>(G) : pick_mixed_g<128, false>(G));
+  mixed_fn kern = dtype == PA_F16 ? pick_mixed<PA_F16>(head_dim, wide, G)
+                                  : pick_mixed<PA_BF16>(head_dim, wide, G);
   // Prefill workgroups: at most one per compute unit, each looping over the tile list;
   // fewer when the batch cannot hold that many tiles (sum over prefill sequences of
   // ceil(Lq / BM) <= total_q / BM + number of such sequences).
@@ -200,8 +207,13 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
                      w.cuc, head_waves, pl.Wt);
   int st = check_launch(fn);
   if (st) return st;
-  hipLaunchKernelGGL((merge_balanced_kernel<true, true>), dim3(num_q_heads, num_seqs),
-                     dim3(head_dim), 0, s, out, w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q,
-                     num_seqs, num_q_heads, head_dim, pl.Wt);
+  if (dtype == PA_F16)
+    hipLaunchKernelGGL((merge_balanced_kernel<PA_F16, true>), dim3(num_q_heads, num_seqs),
+                       dim3(head_dim), 0, s, out, w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q,
+                       num_seqs, num_q_heads, head_dim, pl.Wt);
+  else
+    hipLaunchKernelGGL((merge_balanced_kernel<PA_BF16, true>), dim3(num_q_heads, num_seqs),
+                       dim3(head_dim), 0, s, out, w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q,
+                       num_seqs, num_q_heads, head_dim, pl.Wt);
   return check_launch("pa_attention_mixed merge");
 }

@@ -29,7 +29,7 @@
 
 namespace pa {
 
-template <int D, int G, bool WIDE>
+template <int D, int G, bool WIDE, int ET>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_table, int maxb,
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   // tiles that read the same K/V rows hit the same L2.
   const int nx = gridDim.x, ny = gridDim.y;
   const int lid = xcd_local_id(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
-  prefill_body<D, G, WIDE, false>(lid % nx, (lid / nx) % ny, lid / (nx * ny), out, q, kc, vc,
+  prefill_body<D, G, WIDE, false, ET>(lid % nx, (lid / nx) % ny, lid / (nx * ny), out, q, kc, vc,
                                   block_table, maxb, cu_q, cu_k, total_q, num_blocks, bs_log2, HQ,
                                   HKV, scale_log2, causal);
 }
@@ -48,20 +48,26 @@ typedef void (*prefill_fn)(uint16_t*, const uint16_t*, const uint16_t*, const ui
                            const int32_t*, int, const int32_t*, const int32_t*, int, int, int, int,
                            int, float, int);
 
-template <int D, bool WIDE>
+template <int D, bool WIDE, int ET>
 static prefill_fn pick_prefill_g(int G) {
   switch (G) {
-    case 1: return prefill_kernel<D, 1, WIDE>;
-    case 2: return prefill_kernel<D, 2, WIDE>;
-    case 3: return prefill_kernel<D, 3, WIDE>;
-    case 4: return prefill_kernel<D, 4, WIDE>;
-    case 5: return prefill_kernel<D, 5, WIDE>;
-    case 6: return prefill_kernel<D, 6, WIDE>;
-    case 7: return prefill_kernel<D, 7, WIDE>;
-    case 8: return prefill_kernel<D, 8, WIDE>;
-    case 16: return prefill_kernel<D, 16, WIDE>;
+    case 1: return prefill_kernel<D, 1, WIDE, ET>;
+    case 2: return prefill_kernel<D, 2, WIDE, ET>;
+    case 3: return prefill_kernel<D, 3, WIDE, ET>;
+    case 4: return prefill_kernel<D, 4, WIDE, ET>;
+    case 5: return prefill_kernel<D, 5, WIDE, ET>;
+    case 6: return prefill_kernel<D, 6, WIDE, ET>;
+    case 7: return prefill_kernel<D, 7, WIDE, ET>;
+    case 8: return prefill_kernel<D, 8, WIDE, ET>;
+    case 16: return prefill_kernel<D, 16, WIDE, ET>;
   }
   return nullptr;
+}
+
+template <int ET>
+static prefill_fn pick_prefill(int D, bool wide, int G) {
+  if (D == 64) return wide ? pick_prefill_g<64, true, ET>(G) : pick_prefill_g<64, false, ET>(G);
+  return wide ? pick_prefill_g<128, true, ET>(G) : pick_prefill_g<128, false, ET>(G);
 }
 
 }  // namespace pa
@@ -82,7 +88,8 @@ extern "C" int pa_prefill_paged(void* out, const void* q, const void* k_cache, c
   if (num_q_heads % num_kv_heads)
     return fail(PA_ERR_SHAPE, "pa_prefill_paged: q_heads %d not a multiple of kv_heads %d",
                 num_q_heads, num_kv_heads);
-  if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_paged: dtype must be PA_BF16");
+  if (dtype != PA_BF16 && dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill_paged: dtype must be PA_BF16 or PA_F16");
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill_paged: head_dim %d (64 or 128)", head_dim);
   if (!is_pow2(block_size) || block_size < 8 || block_size > 1024)
@@ -105,8 +112,8 @@ extern "C" int pa_prefill_paged(void* out, const void* q, const void* k_cache, c
     return fail(PA_ERR_ALIGN, "pa_prefill_paged: pointers must be 16-byte aligned");
   const int G = num_q_heads / num_kv_heads;
   const bool wide = block_size >= kPrefillKeys;
-  prefill_fn fn = head_dim == 64 ? (wide ? pick_prefill_g<64, true>(G) : pick_prefill_g<64, false>(G))
-                                 : (wide ? pick_prefill_g<128, true>(G) : pick_prefill_g<128, false>(G));
+  prefill_fn fn = dtype == PA_F16 ? pick_prefill<PA_F16>(head_dim, wide, G)
+                                  : pick_prefill<PA_BF16>(head_dim, wide, G);
   if (!fn) return fail(PA_ERR_UNSUPPORTED, "pa_prefill_paged: GQA group %d (1-8 or 16)", G);
   const int BM = kPrefillRows / G;
   dim3 grid((max_seqlen_q + BM - 1) / BM, num_kv_heads, num_seqs);

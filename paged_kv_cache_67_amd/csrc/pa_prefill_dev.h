@@ -22,9 +22,31 @@ constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is
 // exp2(-inf - m) = 0 rather than NaN, and a key half that never sees a key merges with weight 0.
 constexpr float kNoMax = -1.0e30f;
 
-__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// The 16-bit element types of the matrix-core path (ET = pa_dtype): operand vector,
+// v_mfma_f32_16x16x32_{bf16,f16}, fp32 -> element conversion (round to nearest even) and
+// the element's bits.
+template <int ET>
+struct Mfma;
+template <>
+struct Mfma<PA_BF16> {
+  typedef bf16x8_t v8;
+  __device__ static f32x4_t mma(const v8& a, const v8& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __bf16 cvt(float x) { return (__bf16)x; }
+  __device__ static uint16_t bits(float x) { return f32_to_bf16(x); }
+};
+template <>
+struct Mfma<PA_F16> {
+  typedef f16x8_t v8;
+  __device__ static f32x4_t mma(const v8& a, const v8& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static _Float16 cvt(float x) { return (_Float16)x; }
+  __device__ static uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+};
 
 // Max over the four lanes l, l^16, l^32, l^48 (the lanes that hold one query's scores), on
 // gfx950's lane-swap instructions instead of an LDS round trip.
@@ -57,13 +79,15 @@ __device__ __forceinline__ float max_over_groups(float x) {
 // The body of one workgroup item: query tile qt of sequence b for KV head g.  MIXED: the
 // batch also holds decode rows (sequences with one query), which the decode side of the
 // launch handles; such a sequence is skipped here.
-template <int D, int G, bool WIDE, bool MIXED>
+template <int D, int G, bool WIDE, bool MIXED, int ET>
 __device__ __forceinline__ void prefill_body(
     int qt, int g, int b, uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int total_q, int num_blocks, int bs_log2, int HQ, int HKV,
     float scale_log2, int causal) {
+  using M = Mfma<ET>;
+  using v8 = typename M::v8;
   constexpr int BM = kPrefillRows / G;  // positions per workgroup
   constexpr int BN = kPrefillKeys;
   constexpr int NT = kPrefillThreads;
@@ -124,14 +148,14 @@ __device__ __forceinline__ void prefill_body(
   // B operand of S^T: this lane's queries, d = 32ds + 8*grp + 0..7.  A row past the
   // sequence reads a clamped (valid) token instead: rows never mix and such a row is not
   // stored, and unconditional loads keep the compiler from draining the queue after each.
-  bf16x8_t qreg[2][DS];
+  v8 qreg[2][DS];
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
     const int64_t tok = min(max(qtok[qg], (int64_t)0), (int64_t)total_q - 1);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
       qreg[qg][ds] = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(q + (tok * HQ + hq[qg]) * D + 32 * ds + 8 * grp));
+          v8, *reinterpret_cast<const uint4*>(q + (tok * HQ + hq[qg]) * D + 32 * ds + 8 * grp));
   }
 
   // s_bt[i] holds block-table entry btb + i for i < nv = min(nblk - btb, kBtCache), each
@@ -237,10 +261,9 @@ __device__ __forceinline__ void prefill_body(
       s[1][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(&K[(krow + 16 * kb) * P + 32 * ds + 8 * grp]);
-        s[0][kb] = mfma16(a, qreg[0][ds], s[0][kb]);
-        s[1][kb] = mfma16(a, qreg[1][ds], s[1][kb]);
+        const v8 a = *reinterpret_cast<const v8*>(&K[(krow + 16 * kb) * P + 32 * ds + 8 * grp]);
+        s[0][kb] = M::mma(a, qreg[0][ds], s[0][kb]);
+        s[1][kb] = M::mma(a, qreg[1][ds], s[1][kb]);
       }
     }
   };
@@ -255,9 +278,9 @@ __device__ __forceinline__ void prefill_body(
     lsum[qg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     m[qg] = kNoMax;
   }
-  bf16x8_t ones;
+  v8 ones;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
+  for (int i = 0; i < 8; ++i) ones[i] = M::cvt(1.0f);
 
   // Transposing read: lane p = a + 4t of group grp addresses key 4*grp + t (+16 for the
   // second half) of the key half at d column 4a (+16db); lane 4a + c then holds
@@ -306,13 +329,13 @@ __device__ __forceinline__ void prefill_body(
 
     f32x4_t sn[2][2];
     scores(sKV[(t + 1) & 1], sn);
-    bf16x8_t pb[2];
+    v8 pb[2];
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pb[qg][i] = (__bf16)fast_exp2(fmaf(sc[qg][0][i], scale_log2, -m[qg]));
-        pb[qg][4 + i] = (__bf16)fast_exp2(fmaf(sc[qg][1][i], scale_log2, -m[qg]));
+        pb[qg][i] = M::cvt(fast_exp2(fmaf(sc[qg][0][i], scale_log2, -m[qg])));
+        pb[qg][4 + i] = M::cvt(fast_exp2(fmaf(sc[qg][1][i], scale_log2, -m[qg])));
       }
 
     const uint16_t* V = sKV[2 + (t & 1)] + tr_off;
@@ -322,13 +345,12 @@ __device__ __forceinline__ void prefill_body(
           (v4i16_t __attribute__((address_space(3)))*)(V + 16 * db));
       const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (v4i16_t __attribute__((address_space(3)))*)(V + 16 * db + 16 * P));
-      const bf16x8_t a =
-          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[0][db] = mfma16(a, pb[0], o[0][db]);
-      o[1][db] = mfma16(a, pb[1], o[1][db]);
+      const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[0][db] = M::mma(a, pb[0], o[0][db]);
+      o[1][db] = M::mma(a, pb[1], o[1][db]);
     }
-    lsum[0] = mfma16(ones, pb[0], lsum[0]);
-    lsum[1] = mfma16(ones, pb[1], lsum[1]);
+    lsum[0] = M::mma(ones, pb[0], lsum[0]);
+    lsum[1] = M::mma(ones, pb[1], lsum[1]);
 
     // K_{t+2} into the K buffer read last iteration, V_{t+1} into the V buffer read last
     // iteration (stale tiles past the end are written but never read).
@@ -412,8 +434,8 @@ __device__ __forceinline__ void prefill_body(
       for (int i = 0; i < 4; ++i)
         r[i] = (o[qg][db][i] * a0 + mO[((rg * 2 + qg) * 4 * DB + 4 * db + i) * 64 + lane] * a1) * inv;
       uint2 pk;
-      pk.x = uint32_t(f32_to_bf16(r[0])) | (uint32_t(f32_to_bf16(r[1])) << 16);
-      pk.y = uint32_t(f32_to_bf16(r[2])) | (uint32_t(f32_to_bf16(r[3])) << 16);
+      pk.x = uint32_t(M::bits(r[0])) | (uint32_t(M::bits(r[1])) << 16);
+      pk.y = uint32_t(M::bits(r[2])) | (uint32_t(M::bits(r[3])) << 16);
       *reinterpret_cast<uint2*>(dst + 16 * db + 4 * grp) = pk;
     }
   }

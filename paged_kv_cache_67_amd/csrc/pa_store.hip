@@ -89,7 +89,7 @@ extern "C" int pa_store_kv(const void* key, const void* value, int64_t key_token
   if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0)
     return fail(PA_ERR_SHAPE, "pa_store_kv: bad size (tokens %d, blocks %d, kv_heads %d, dim %d)",
                 num_tokens, num_blocks, num_kv_heads, head_dim);
-  if (dtype != PA_F32 && dtype != PA_BF16)
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16)
     return fail(PA_ERR_UNSUPPORTED, "pa_store_kv: dtype %d", (int)dtype);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_store_kv: head_dim %d (64 or 128)", head_dim);

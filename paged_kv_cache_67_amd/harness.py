@@ -16,9 +16,11 @@ from . import _binding as pa
 
 
 def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
-    """Storage-dtype numpy array (bf16 as uint16 bits, or float32) -> device tensor."""
+    """Storage-dtype numpy array (bf16 as uint16 bits, float16 or float32) -> device tensor."""
     if dtype == "bf16":
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16))
     else:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(device)
@@ -39,7 +41,7 @@ class DeviceWorkload:
         self.w = w
         self.device = torch.device(device)
         dev = self.device
-        self.tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.tdtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         self.block_table = i32(w.block_table)
         self.seq_lens_k = i32(w.seq_lens_k)

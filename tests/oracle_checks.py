@@ -400,3 +400,14 @@ def check_bf16_widening(ns):
 
 
 ALL_CHECKS.append(check_bf16_widening)
+
+
+def check_f16_widening(ns):
+    """fp16 values widen exactly as torch's own float16 -> float64 conversion."""
+    t = (torch.randn(4096, generator=torch.Generator().manual_seed(4)) * 7).to(torch.float16)
+    vals = t.numpy()
+    got = _oracle.to_f64(vals, "f16") if ns.to_f64 is None else ns.to_f64(vals, "f16")
+    assert np.array_equal(got, t.double().numpy())
+
+
+ALL_CHECKS.append(check_f16_widening)

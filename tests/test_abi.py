@@ -78,6 +78,10 @@ def test_null_and_shape_errors(L):
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 0, None) == 3
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 9, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 1, None) == 2
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 1, None) == 1
+    assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 2, None) == 1  # fp16
+    assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 3, None) == 3
+    assert L.pa_decode(None, None, None, None, None, 4, None, 2, 0, 8, 16, 4, 2, 64, 0.1, 2, 0, None, 0, None) == 1  # fp16
+    assert L.pa_decode(None, None, None, None, None, 4, None, 2, 0, 8, 16, 4, 2, 64, 0.1, 3, 0, None, 0, None) == 3
     # pa_attention_mixed: bf16 only, supported groups, batch limit, null checks; empty is a no-op
     mixed = lambda seqs, tq, mq, mk, hq, hkv, d, dt: L.pa_attention_mixed(
         None, None, None, None, None, 4, None, None, seqs, tq, mq, mk, 8, 16, hq, hkv, d, 0.1, dt,

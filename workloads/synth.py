@@ -1,9 +1,9 @@
 """Seeded workload generator (lengths, block placement, random values).
 
 Storage dtypes travel as raw bits so that the oracle and the GPU receive the
-very same values: ``f32`` arrays are ``numpy.float32`` and ``bf16`` arrays are
-``numpy.uint16`` holding bfloat16 bit patterns (rounded to nearest-even from
-an fp32 N(0,1) draw).
+very same values: ``f32`` arrays are ``numpy.float32``, ``f16`` arrays are
+``numpy.float16`` and ``bf16`` arrays are ``numpy.uint16`` holding bfloat16 bit
+patterns (both 16-bit types rounded to nearest-even from an fp32 N(0,1) draw).
 
 Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this
 order):
@@ -51,11 +51,13 @@ def nan_bits(dtype: str):
         return np.uint16(0x7FC0)
     if dtype == "f32":
         return np.float32(np.nan)
+    if dtype == "f16":
+        return np.float16(np.nan)
     raise ValueError(dtype)
 
 
 def storage_np_dtype(dtype: str):
-    return {"bf16": np.uint16, "f32": np.float32}[dtype]
+    return {"bf16": np.uint16, "f32": np.float32, "f16": np.float16}[dtype]
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -64,7 +66,7 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     for s in range(0, n, _CHUNK):
         e = min(n, s + _CHUNK)
         x = rng.standard_normal(e - s, dtype=np.float32)
-        out[s:e] = bf16_bits_from_f32(x) if dtype == "bf16" else x
+        out[s:e] = bf16_bits_from_f32(x) if dtype == "bf16" else x  # f16: numpy rounds to nearest even
     return out.reshape(shape)
 
 
@@ -132,7 +134,7 @@ class Workload:
     @property
     def kv_bytes_per_token(self) -> int:
         """Bytes of K plus V one token occupies in one layer's pool."""
-        elt = 2 if self.dtype == "bf16" else 4
+        elt = 4 if self.dtype == "f32" else 2
         return 2 * self.num_kv_heads * self.head_dim * elt
 
 
