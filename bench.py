@@ -289,6 +289,30 @@ def time_f16_decode(w, dw, args):
     return {"workload": w.name, **res}
 
 
+def time_copy_blocks(w, dw, args):
+    """pa_copy_blocks over the decode pool: copy-on-write copies of n whole blocks (K and
+    V), sources and destinations drawn without overlap, by HIP graph replay.  Bytes moved:
+    n x block bytes x 2 pools, read once and written once."""
+    import torch
+
+    import paged_kv_cache_67_amd as pk
+
+    rng = np.random.default_rng(67007)
+    block_bytes = w.block_size * w.num_kv_heads * w.head_dim * 2
+    res = {}
+    for n in sorted({16, min(256, w.num_blocks // 2), w.num_blocks // 2}):
+        ids = rng.permutation(w.num_blocks)[:2 * n].astype(np.int32)
+        pairs = torch.from_numpy(ids.reshape(2, n).T.copy()).cuda()
+        us = _graph_us(lambda: pk.pa_copy_blocks(dw.k_cache, dw.v_cache, pairs),
+                       max(20, args.steps // 5))
+        moved = 4 * n * block_bytes
+        gbs = moved / (us * 1e-6) / 1e9
+        res[str(n)] = {"us": round(us, 2), "bytes": moved, "GBps": round(gbs, 1)}
+        log(f"pa_copy_blocks: {n} blocks of {block_bytes} B (K and V): {us:.1f} us, "
+            f"{gbs:.1f} GB/s")
+    return {"workload": w.name, "block_bytes": block_bytes, "by_pairs": res}
+
+
 def time_mixed(args):
     """A mixed serving step: 256 decode rows + 8 chunks of 256 new tokens over 1024 cached,
     one pa_attention_mixed call against separate pa_decode + pa_prefill_paged calls on the
@@ -509,6 +533,7 @@ def main():
         extra["f16_decode"] = time_f16_decode(w, dw, args)
     if not args.no_graphs:
         extra["graphs"] = time_graphs(w, dw, args)
+    extra["copy_blocks"] = time_copy_blocks(w, dw, args)  # overwrites pool blocks: runs last
     del dw
     torch.cuda.empty_cache()
     if not args.no_prefill:

@@ -66,7 +66,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 3, /* dtype / head_dim / block_size / head ratio without a kernel */
   PA_ERR_ALIGN = 4,       /* a pointer or stride breaks the 16-byte alignment rule */
   PA_ERR_WORKSPACE = 5,   /* workspace smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = 6          /* the HIP runtime rejected a launch */
+  PA_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
+  PA_ERR_CAPACITY = 7     /* block manager: not enough free blocks */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
@@ -301,6 +302,70 @@ int pa_attention_mixed(void* out, const void* q, const void* k_cache, const void
                        int32_t max_seqlen_k, int32_t num_blocks, int32_t block_size,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
                        pa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole pool blocks (K and V), e.g. for copy-on-write.
+ *
+ * For each pair p: blocks block_pairs[2p] (source) -> block_pairs[2p+1]
+ * (destination) of both pools, all block_size x num_kv_heads x head_dim
+ * elements.  Block sharing and copy-on-write follow [KVblog] 2.2 (sequences
+ * share a physical block through reference counts; a write into a shared block
+ * first copies it).
+ *
+ *   block_pairs  in   DEVICE int32 [num_pairs][2]; a pair with an id outside
+ *                     [0, num_blocks) or src == dst is skipped
+ *
+ * Destinations must be distinct and must not be sources of another pair.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, pa_dtype dtype, void* stream);
+
+/*
+ * Host-side block manager with a chain-hash prefix cache ([KVblog] 3.3, 3.4;
+ * [Lab] B.6).  Pure host code: it hands out block ids and block tables and
+ * never touches device memory.  A handle is used from one thread at a time.
+ *
+ * pa_chain_hash: the fingerprint of one full block -- XXH64 (seed 0) over the
+ *   previous block's fingerprint (8 bytes little-endian, only if has_prefix)
+ *   followed by the block's token ids as 64-bit little-endian integers.
+ * pa_bm_create / pa_bm_destroy: a manager of num_blocks >= 1 blocks of
+ *   block_size >= 2 tokens (NULL on bad sizes).
+ * pa_bm_allocate: admit a prompt (needs ceil(n / block_size) free blocks, else
+ *   -PA_ERR_CAPACITY); its full blocks are looked up by fingerprint (the last
+ *   block is always computed), a hit on a block in use adds a reference
+ *   (REUSE), a hit on a freed block takes it back (REACTIVATE), the first miss
+ *   ends the hits; returns a sequence handle >= 0 or -status.
+ * pa_bm_append: one generated token; allocates a block when the token opens
+ *   one, registers a block's fingerprint when the token fills it, and when the
+ *   last block is shared with a fork, replaces it by a private copy and reports
+ *   the pair (*cow_src, *cow_dst) for pa_copy_blocks (both -1 otherwise).
+ * pa_bm_fork: a new sequence sharing all blocks of `seq` (one more reference
+ *   each).
+ * pa_bm_free: drop one reference per block, last block first; blocks at zero
+ *   return to the back of the free list and keep their fingerprint until
+ *   reallocated.  Unknown handles give -PA_ERR_SHAPE (PA_ERR_SHAPE from the
+ *   int-returning calls).
+ * Queries: block table (returns its length, copies up to capacity entries),
+ *   sequence length, cached prompt tokens, a block's reference count, free
+ *   blocks; negative status on a bad handle.
+ */
+typedef struct pa_block_manager pa_block_manager;
+uint64_t pa_chain_hash(const int32_t* token_ids, int32_t num_tokens, int32_t has_prefix,
+                       uint64_t prefix);
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+int64_t pa_bm_allocate(pa_block_manager* bm, const int32_t* token_ids, int32_t num_tokens);
+int pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t token_id, int32_t* cow_src,
+                 int32_t* cow_dst);
+int64_t pa_bm_fork(pa_block_manager* bm, int64_t seq);
+int pa_bm_free(pa_block_manager* bm, int64_t seq);
+int32_t pa_bm_block_table(const pa_block_manager* bm, int64_t seq, int32_t* out,
+                          int32_t capacity);
+int32_t pa_bm_seq_len(const pa_block_manager* bm, int64_t seq);
+int32_t pa_bm_num_cached_tokens(const pa_block_manager* bm, int64_t seq);
+int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block_id);
+int32_t pa_bm_num_free_blocks(const pa_block_manager* bm);
 
 #ifdef __cplusplus
 }

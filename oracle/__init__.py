@@ -11,6 +11,7 @@ of each function (what pins it) is listed in ``oracle.paged_attention``.
 """
 
 from .paged_attention import (  # noqa: F401
+    copy_blocks,
     decode,
     decode_partials,
     gather_rows,

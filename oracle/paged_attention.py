@@ -113,6 +113,24 @@ def store_kv(k_pool, v_pool, key, value, slots) -> None:
         v_pool[s // bs, s % bs] = value[t]
 
 
+def copy_blocks(k_pool, v_pool, pairs) -> None:
+    """Copy whole blocks ``src -> dst`` of both pools, in place, for each (src, dst) pair.
+
+    [KVblog] 2.2: sequences that share a physical block write into it only after
+    copying it to a block of their own (copy-on-write).  A pair naming a block
+    outside the pool, or with src == dst, copies nothing.  Destinations are
+    distinct and are not sources of other pairs, so the order of the pairs does
+    not matter.  A pure copy, so the result is bit-exact.
+    """
+    nb = k_pool.shape[0]
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        src, dst = int(src), int(dst)
+        if not (0 <= src < nb and 0 <= dst < nb) or src == dst:
+            continue
+        k_pool[dst] = k_pool[src]
+        v_pool[dst] = v_pool[src]
+
+
 # ---------------------------------------------------------------------------
 # reading a sequence back through its block table
 

@@ -11,10 +11,13 @@ from ._binding import (  # noqa: F401
     PA_BF16,
     PA_F16,
     PA_F32,
+    BlockManager,
     PAError,
     lib,
     lib_path,
     pa_attention_mixed,
+    pa_chain_hash,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_merge,
     pa_decode_partitions,

@@ -18,9 +18,10 @@ _lib = None
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-          4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP"}
+          4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
 
 _i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+_u64, _pi32 = C.c_uint64, C.POINTER(C.c_int32)
 
 # name -> (restype, argtypes); mirrors include/pa.h
 SIGNATURES = {
@@ -42,6 +43,19 @@ SIGNATURES = {
     "pa_attention_mixed": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp, _sz,
                                      _vp]),
+    "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_chain_hash": (_u64, [_pi32, _i32, _i32, _u64]),
+    "pa_bm_create": (_vp, [_i32, _i32]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_allocate": (_i64, [_vp, _pi32, _i32]),
+    "pa_bm_append": (C.c_int, [_vp, _i64, _i32, _pi32, _pi32]),
+    "pa_bm_fork": (_i64, [_vp, _i64]),
+    "pa_bm_free": (C.c_int, [_vp, _i64]),
+    "pa_bm_block_table": (_i32, [_vp, _i64, _pi32, _i32]),
+    "pa_bm_seq_len": (_i32, [_vp, _i64]),
+    "pa_bm_num_cached_tokens": (_i32, [_vp, _i64]),
+    "pa_bm_ref_count": (_i32, [_vp, _i32]),
+    "pa_bm_num_free_blocks": (_i32, [_vp]),
 }
 
 
@@ -224,3 +238,88 @@ def pa_attention_mixed(out, q, k_cache, v_cache, block_table, cu_seqlens_q, cu_s
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k), NB, BS,
         HQ, HKV, D, float(scale), _dtype(q), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy blocks block_pairs[p, 0] -> block_pairs[p, 1] of both pools (device int32 [P, 2])."""
+    NB, BS, HKV, D = k_cache.shape
+    assert v_cache.shape == k_cache.shape and k_cache.is_contiguous() and v_cache.is_contiguous()
+    assert v_cache.dtype == k_cache.dtype
+    assert block_pairs.dtype == torch.int32 and block_pairs.is_contiguous()
+    assert block_pairs.dim() == 2 and block_pairs.shape[1] == 2
+    _check("pa_copy_blocks", lib().pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0], NB, BS, HKV, D,
+        _dtype(k_cache), _stream(stream)))
+
+
+def _host_i32(values):
+    arr = (C.c_int32 * max(1, len(values)))(*values)
+    return arr
+
+
+def pa_chain_hash(token_ids, prefix=None) -> int:
+    """Fingerprint of one block of token ids, chained on the previous block's (None: first)."""
+    arr = _host_i32(list(token_ids))
+    return lib().pa_chain_hash(arr, len(token_ids), 0 if prefix is None else 1,
+                               0 if prefix is None else int(prefix))
+
+
+class BlockManager:
+    """Handle on the library's host-side block manager (pa_bm_*); marshalling only."""
+
+    def __init__(self, num_blocks, block_size):
+        self._h = lib().pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PAError("pa_bm_create", 2, pa_last_error())
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _seq(self, fn, r):
+        if r < 0:
+            raise PAError(fn, -r, pa_last_error())
+        return r
+
+    def allocate(self, token_ids) -> int:
+        arr = _host_i32(list(token_ids))
+        return self._seq("pa_bm_allocate", lib().pa_bm_allocate(self._h, arr, len(token_ids)))
+
+    def append(self, seq, token_id):
+        """Returns the (src, dst) copy-on-write pair, or None."""
+        src, dst = C.c_int32(-1), C.c_int32(-1)
+        _check("pa_bm_append", lib().pa_bm_append(self._h, seq, int(token_id), C.byref(src),
+                                                  C.byref(dst)))
+        return None if src.value < 0 else (src.value, dst.value)
+
+    def fork(self, seq) -> int:
+        return self._seq("pa_bm_fork", lib().pa_bm_fork(self._h, seq))
+
+    def free(self, seq):
+        _check("pa_bm_free", lib().pa_bm_free(self._h, seq))
+
+    def block_table(self, seq):
+        n = self._seq("pa_bm_block_table", lib().pa_bm_block_table(self._h, seq, None, 0))
+        out = (C.c_int32 * max(1, n))()
+        lib().pa_bm_block_table(self._h, seq, out, n)
+        return list(out[:n])
+
+    def seq_len(self, seq) -> int:
+        return self._seq("pa_bm_seq_len", lib().pa_bm_seq_len(self._h, seq))
+
+    def num_cached_tokens(self, seq) -> int:
+        return self._seq("pa_bm_num_cached_tokens", lib().pa_bm_num_cached_tokens(self._h, seq))
+
+    def ref_count(self, block_id) -> int:
+        return self._seq("pa_bm_ref_count", lib().pa_bm_ref_count(self._h, int(block_id)))
+
+    def num_free_blocks(self) -> int:
+        return lib().pa_bm_num_free_blocks(self._h)

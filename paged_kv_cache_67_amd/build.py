@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["pa_status.cpp", "pa_store.hip", "pa_decode.hip", "pa_prefill.hip", "pa_mixed.hip"]
+SOURCES = ["pa_status.cpp", "pa_blocks.cpp", "pa_store.hip", "pa_decode.hip", "pa_prefill.hip",
+           "pa_mixed.hip"]
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 

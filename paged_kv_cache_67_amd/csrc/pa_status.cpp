@@ -41,6 +41,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_ALIGN: return "misaligned pointer or stride";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_CAPACITY: return "not enough free blocks";
     default: return "unknown status";
   }
 }

@@ -1,4 +1,4 @@
-// a1 slot addressing and a2 K/V scatter into the paged pool (gfx950).
+// a1 slot addressing, a2 K/V scatter into the paged pool, and whole-block copies (gfx950).
 //
 // Slot addressing follows "大模型推理引擎学习入门-2 ... nano-vllm 的 KV Cache 以及
 // Paged Attention" (juejin.cn) section 3.5: slot = block_table[p / B] * B + p % B.
@@ -51,6 +51,29 @@ __global__ __launch_bounds__(256) void store_kv_kernel(
     const uint4 v = reinterpret_cast<const uint4*>(value + t * value_stride_bytes)[c];
     reinterpret_cast<uint4*>(kc + (int64_t)s * row_bytes)[c] = k;
     reinterpret_cast<uint4*>(vc + (int64_t)s * row_bytes)[c] = v;
+  }
+}
+
+// Whole-block copy of both pools for a list of (src, dst) block pairs.  blockIdx.y strides
+// over the pairs, blockIdx.x x threads over the 16-byte chunks of one block; a pair with an
+// id out of range, or src == dst, copies nothing.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* kc, char* vc,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int num_pairs, int num_blocks,
+                                                          int64_t block_bytes, int chunks) {
+  for (int p = blockIdx.y; p < num_pairs; p += gridDim.y) {
+    const int src = pairs[2 * p], dst = pairs[2 * p + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) continue;
+    const uint4* ks = reinterpret_cast<const uint4*>(kc + (int64_t)src * block_bytes);
+    const uint4* vs = reinterpret_cast<const uint4*>(vc + (int64_t)src * block_bytes);
+    uint4* kd = reinterpret_cast<uint4*>(kc + (int64_t)dst * block_bytes);
+    uint4* vd = reinterpret_cast<uint4*>(vc + (int64_t)dst * block_bytes);
+    for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += gridDim.x * blockDim.x) {
+      const uint4 k = ks[c];
+      const uint4 v = vs[c];
+      kd[c] = k;
+      vd[c] = v;
+    }
   }
 }
 
@@ -118,4 +141,30 @@ extern "C" int pa_store_kv(const void* key, const void* value, int64_t key_token
                      value_token_stride * eb, (char*)k_cache, (char*)v_cache, slot_mapping, items,
                      row_chunks, (int64_t)num_blocks * block_size, row_bytes);
   return check_launch("pa_store_kv");
+}
+
+extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                              int32_t num_pairs, int32_t num_blocks, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                              void* stream) {
+  clear_error();
+  if (num_pairs < 0 || num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: bad size (pairs %d, blocks %d, block %d, kv_heads "
+                "%d, dim %d)", num_pairs, num_blocks, block_size, num_kv_heads, head_dim);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: dtype %d", (int)dtype);
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elt_bytes(dtype);
+  if (block_bytes % 16 || block_bytes / 16 > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: block of %lld bytes (a multiple of 16 below "
+                "32 GiB)", (long long)block_bytes);
+  if (num_pairs == 0 || num_blocks == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_NULL, "pa_copy_blocks: null pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_ALIGN, "pa_copy_blocks: pools must be 16-byte aligned");
+  const int chunks = int(block_bytes / 16);
+  const int gx = (chunks + 255) / 256;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx < 1024 ? gx : 1024, num_pairs < 65535 ? num_pairs : 65535),
+                     dim3(256), 0, (hipStream_t)stream, (char*)k_cache, (char*)v_cache, block_pairs,
+                     num_pairs, num_blocks, block_bytes, chunks);
+  return check_launch("pa_copy_blocks");
 }

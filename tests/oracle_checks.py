@@ -34,7 +34,7 @@ def real_oracle():
         decode=_oracle.decode, prefill=_oracle.prefill, slot_mapping=_oracle.slot_mapping,
         store_kv=_oracle.store_kv, decode_partials=_oracle.decode_partials,
         lse_merge=_oracle.lse_merge, gather_rows=_oracle.gather_rows,
-        to_f64=_oracle.to_f64)
+        to_f64=_oracle.to_f64, copy_blocks=_oracle.copy_blocks)
 
 
 # ---------------------------------------------------------------------------
@@ -411,3 +411,26 @@ def check_f16_widening(ns):
 
 
 ALL_CHECKS.append(check_f16_widening)
+
+
+def check_copy_blocks(ns):
+    """Each destination block of both pools holds its source's rows afterwards; every
+    other block, and every pair naming a block outside the pool or itself, changes
+    nothing (checked against a per-element walk of the pools)."""
+    rng = np.random.default_rng(8)
+    NB, BS, HKV, D = 9, 4, 2, 8
+    kp, vp = _rand(rng, NB, BS, HKV, D), _rand(rng, NB, BS, HKV, D)
+    k0, v0 = kp.copy(), vp.copy()
+    pairs = np.array([[1, 4], [2, 2], [-1, 5], [3, NB], [7, 6], [0, 8]], dtype=np.int32)
+    ns.copy_blocks(kp, vp, pairs)
+    dest = {4: 1, 6: 7, 8: 0}
+    for blk in range(NB):
+        for r in range(BS):
+            for h in range(HKV):
+                for d in range(D):
+                    src = dest.get(blk, blk)
+                    assert kp[blk, r, h, d] == k0[src, r, h, d], (blk, r, h, d)
+                    assert vp[blk, r, h, d] == v0[src, r, h, d], (blk, r, h, d)
+
+
+ALL_CHECKS.append(check_copy_blocks)

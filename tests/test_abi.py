@@ -140,3 +140,13 @@ def test_workspace_size_closed_form(L):
     # the mixed launch uses the balanced bf16 layout over all its sequences
     assert L.pa_mixed_workspace_size(264, 16, 8, 128, 4096) == 16 * 256 * 2 * 130 * 4 + 265 * 4
     assert L.pa_mixed_workspace_size(5000, 16, 8, 128, 4096) == 0
+
+
+def test_copy_blocks_validation(L):
+    # (k, v, pairs, num_pairs, num_blocks, block_size, kv_heads, head_dim, dtype, stream)
+    assert L.pa_copy_blocks(None, None, None, 0, 8, 16, 2, 64, 1, None) == 0  # nothing to copy
+    assert L.pa_copy_blocks(None, None, None, 3, 8, 16, 2, 64, 1, None) == 1
+    assert L.pa_copy_blocks(None, None, None, -1, 8, 16, 2, 64, 1, None) == 2
+    assert L.pa_copy_blocks(None, None, None, 3, 8, 16, 2, 64, 9, None) == 3
+    assert L.pa_copy_blocks(None, None, None, 3, 8, 1, 1, 3, 0, None) == 3  # 12-byte blocks
+    assert "multiple of 16" in pk.pa_last_error()

@@ -40,6 +40,9 @@ MUTANTS = [
     ("partial drops last key", "lo, hi = p * P, min((p + 1) * P, L)", "lo, hi = p * P, min((p + 1) * P, L - 1)"),
     ("merge forgets l", "/ (w @ l[b, h, :n].astype(np.float64))", "/ np.sum(w)"),
     ("bf16 widening shift", "<< np.uint32(16)", "<< np.uint32(15)"),
+    ("copy_blocks copies K only", "        v_pool[dst] = v_pool[src]\n", "\n"),
+    ("copy_blocks direction swapped", "k_pool[dst] = k_pool[src]", "k_pool[src] = k_pool[dst]"),
+    ("copy_blocks keeps out-of-range pairs", "if not (0 <= src < nb and 0 <= dst < nb) or src == dst:", "if src == dst:"),
 ]
 
 
@@ -51,7 +54,7 @@ def _mutant_namespace(old, new):
     return types.SimpleNamespace(
         decode=mod.decode, prefill=mod.prefill, slot_mapping=mod.slot_mapping,
         store_kv=mod.store_kv, decode_partials=mod.decode_partials, lse_merge=mod.lse_merge,
-        gather_rows=mod.gather_rows, to_f64=mod.to_f64)
+        gather_rows=mod.gather_rows, to_f64=mod.to_f64, copy_blocks=mod.copy_blocks)
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

@@ -18,4 +18,5 @@ from .synth import (  # noqa: F401
     make_mixed,
     make_workload,
     nan_bits,
+    normal_values,
 )

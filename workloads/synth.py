@@ -70,6 +70,11 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return out.reshape(shape)
 
 
+def normal_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0, 1) draws of the given shape in the storage representation of ``dtype``."""
+    return _normal(rng, shape, dtype)
+
+
 @dataclasses.dataclass
 class Workload:
     """One batch of synthetic input for a store + attention step.
