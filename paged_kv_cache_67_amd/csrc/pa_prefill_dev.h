@@ -270,13 +270,14 @@ __device__ __forceinline__ void prefill_body(
 
   f32x4_t o[2][DB];
   f32x4_t lsum[2];
-  float m[2];
+  float m[2], thr[2];
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[qg][db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     lsum[qg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     m[qg] = kNoMax;
+    thr[qg] = -INFINITY;  // the first unmasked score always moves the max
   }
   v8 ones;
 #pragma unroll
@@ -304,23 +305,22 @@ __device__ __forceinline__ void prefill_body(
             sc[qg][kb][i] = key < row_nk[qg] ? sc[qg][kb][i] : -INFINITY;
           }
     }
-    float mx[2];
-    bool grow[2];
+    // The running max moves only when some score of the row exceeds it by more than
+    // kLazyRescale (log2 units): a per-lane test against thr = (m + kLazyRescale) / scale
+    // decides that, and only then is the row max taken across the row's lanes.
+    float lmx[2];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-      mx[qg] = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx[qg] = fmaxf(mx[qg], sc[qg][kb][i]);
-      mx[qg] = max_over_groups(mx[qg]) * scale_log2;
-      grow[qg] = mx[qg] > m[qg] + kLazyRescale;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow[0] || grow[1])) {
+    for (int qg = 0; qg < 2; ++qg)
+      lmx[qg] = fmaxf(fmaxf(fmaxf(sc[qg][0][0], sc[qg][0][1]), fmaxf(sc[qg][0][2], sc[qg][0][3])),
+                      fmaxf(fmaxf(sc[qg][1][0], sc[qg][1][1]), fmaxf(sc[qg][1][2], sc[qg][1][3])));
+    if (__builtin_amdgcn_ballot_w64(lmx[0] > thr[0] || lmx[1] > thr[1])) {
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
-        const float alpha = grow[qg] ? fast_exp2(m[qg] - mx[qg]) : 1.0f;
-        m[qg] = grow[qg] ? mx[qg] : m[qg];
+        const float mx = max_over_groups(lmx[qg]) * scale_log2;
+        const bool grow = mx > m[qg] + kLazyRescale;
+        const float alpha = grow ? fast_exp2(m[qg] - mx) : 1.0f;
+        m[qg] = grow ? mx : m[qg];
+        thr[qg] = (m[qg] + kLazyRescale) / scale_log2;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qg][db] *= alpha;
         lsum[qg] *= alpha;
