@@ -291,8 +291,9 @@ def time_f16_decode(w, dw, args):
 
 def time_copy_blocks(w, dw, args):
     """pa_copy_blocks over the decode pool: copy-on-write copies of n whole blocks (K and
-    V), sources and destinations drawn without overlap, by HIP graph replay.  Bytes moved:
-    n x block bytes x 2 pools, read once and written once."""
+    V), sources and destinations drawn without overlap, launched back to back between two
+    events (a graph replay costs more than a small copy here).  Bytes moved: n x block
+    bytes x 2 pools, read once and written once."""
     import torch
 
     import paged_kv_cache_67_amd as pk
@@ -303,8 +304,17 @@ def time_copy_blocks(w, dw, args):
     for n in sorted({16, min(256, w.num_blocks // 2), w.num_blocks // 2}):
         ids = rng.permutation(w.num_blocks)[:2 * n].astype(np.int32)
         pairs = torch.from_numpy(ids.reshape(2, n).T.copy()).cuda()
-        us = _graph_us(lambda: pk.pa_copy_blocks(dw.k_cache, dw.v_cache, pairs),
-                       max(20, args.steps // 5))
+        reps = max(20, args.steps // 5)
+        for _ in range(3):
+            pk.pa_copy_blocks(dw.k_cache, dw.v_cache, pairs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            pk.pa_copy_blocks(dw.k_cache, dw.v_cache, pairs)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
         moved = 4 * n * block_bytes
         gbs = moved / (us * 1e-6) / 1e9
         res[str(n)] = {"us": round(us, 2), "bytes": moved, "GBps": round(gbs, 1)}
@@ -406,14 +416,17 @@ def cpu_baseline(w, dw, seconds):
 
 
 PROFILE = os.path.join(ROOT, "profiles", "decode_qwen3-0.6b-b256.md")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_67_amd", "csrc", "pa_decode.hip")
+# The sources the decode first pass is compiled from, hashed in this order.
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_67_amd", "csrc", f)
+               for f in ("pa_decode.hip", "pa_decode_dev.h", "pa_decode_plan.h", "pa_internal.h")]
 
 
 def measured_traffic():
     """HBM bytes per first-pass launch from the committed counter summary.
 
-    The summary records the sha256 of the decode source it was measured on;
-    if the kernel has changed since, the figure no longer applies (None).
+    The summary records the sha256 of the decode sources it was measured on
+    (DECODE_SRCS concatenated); if the kernel has changed since, the figure no
+    longer applies (None).
     """
     import hashlib
     import re
@@ -424,7 +437,10 @@ def measured_traffic():
     m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]{64})", text)
     if not m:
         return None
-    src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        h.update(open(path, "rb").read())
+    src = h.hexdigest()
     return int(m.group(1)) if m.group(2) == src else None
 
 
