@@ -205,8 +205,8 @@ struct DecodeWave {
       bad |= !ok;
       const int64_t base = (int64_t)(ok ? ids[u] : 0) * blk_bytes;
       const uint32_t off = (uint32_t)(t & bs_mask) * row_bytes + lane_off;
-      X.k[u] = *reinterpret_cast<const uint4*>(kc + base + off);
-      X.v[u] = *reinterpret_cast<const uint4*>(vc + base + off);
+      X.k[u] = load_stream16(kc + base + off);  // every K/V byte is read exactly once
+      X.v[u] = load_stream16(vc + base + off);
     }
   }
 

@@ -75,6 +75,15 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte load marked non-temporal (global_load_dwordx4 ... nt): for data read once,
+// such as the K/V rows of a decode pass, it streams past the caches instead of
+// displacing what they hold.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
