@@ -69,10 +69,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* kc, char* vc,
     uint4* kd = reinterpret_cast<uint4*>(kc + (int64_t)dst * block_bytes);
     uint4* vd = reinterpret_cast<uint4*>(vc + (int64_t)dst * block_bytes);
     for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += gridDim.x * blockDim.x) {
-      const uint4 k = ks[c];
-      const uint4 v = vs[c];
-      kd[c] = k;
-      vd[c] = v;
+      // Source and destination are touched once: non-temporal loads and stores.
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + c));
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + c));
+      __builtin_nontemporal_store(k, reinterpret_cast<u32x4*>(kd + c));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(vd + c));
     }
   }
 }
