@@ -15,7 +15,12 @@
 // the sequences with Lq = 1 (each wave one (slice, KV-head tile) of the
 // flattened decode keys).  Workgroups are handed out in launch order, so decode
 // slices fill the compute units as the prefill tiles drain; no workgroup is
-// launched for a decode row's would-be prefill tile.  Decode rows cut by slice
+// launched for a decode row's would-be prefill tile.  When the batch holds decode
+// rows, only the first half of the prefill workgroups (as many per XCD) take tiles
+// and the rest leave at once: the bandwidth-bound decode slices then run on half
+// the chip alongside the latency-bound prefill tiles instead of after them
+// (measured on 256 decode rows + 8 x 256-token chunks: 396 us against 414 us with
+// every compute unit on prefill first).  Decode rows cut by slice
 // boundaries leave partial states in the workspace; a second small launch
 // merges them.
 #include "pa_decode_plan.h"
@@ -39,16 +44,21 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
     // sequence, then KV head, then tile, and handed out so that consecutive items run on
     // one XCD (tiles of one sequence and KV head read the same K/V rows through its L2).
     constexpr int BM = kPrefillRows / G;
-    extern __shared__ int s_items[];  // [B + 1] exclusive prefix sums of tiles per sequence
+    // [B + 1] exclusive prefix sums of tiles per sequence, then a flag: the batch has
+    // decode rows.
+    extern __shared__ int s_items[];
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
       const int seg = (B + 63) / 64;
       const int lo = min(B, lane * seg), hi = min(B, lo + seg);
       int sum = 0;
+      bool dec = false;
       for (int i = lo; i < hi; ++i) {
         const int Lq = cu_q[i + 1] - cu_q[i];
         sum += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
+        dec |= Lq == 1;
       }
+      const bool any_dec = __builtin_amdgcn_ballot_w64(dec) != 0;
       int incl = sum;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -62,10 +72,16 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
         run += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
       }
       if (lane == 63) s_items[B] = incl;
+      if (lane == 0) s_items[B + 1] = any_dec;
     }
     __syncthreads();
     const int items = HKV * lds_uniform(s_items + B);
-    for (int j = xcd_local_id(blockIdx.x, n_pf); j < items; j += n_pf) {
+    // With decode rows in the batch, at most half the compute units take prefill work
+    // (the first blocks, the same number on every XCD); the others leave at once and
+    // their units run decode slices alongside.
+    const int n_use = lds_uniform(s_items + B + 1) ? min(n_pf, kNumCUs / 2) : n_pf;
+    if ((int)blockIdx.x >= n_use) return;
+    for (int j = xcd_local_id(blockIdx.x, n_use); j < items; j += n_use) {
       int lo = 0, hi = B;  // the sequence: largest b with HKV * s_items[b] <= j
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
