@@ -181,6 +181,49 @@ def time_prefill(args):
     return res
 
 
+def time_other_decode(args):
+    """pa_decode (both passes) on the two other decode workloads: Qwen2.5-0.5B shape
+    (batch 64, 14 Q / 2 KV heads, d64, block 16) and the skewed long-context batch (one
+    32768-token sequence and seven of 512).  Each fits in the 256 MB Infinity Cache, so
+    the launches rotate over enough buffer sets (own pools) to touch about 1 GB, one
+    launch per set captured in a HIP graph and replayed between two events."""
+    import torch
+
+    from paged_kv_cache_67_amd import harness
+    from workloads import make_config
+
+    res = {}
+    for idx in (1, 3):
+        w = make_config(idx)
+        kv, q, bt = decode_bytes(w)
+        nbytes = kv + 2 * q + bt
+        pool = 2 * int(np.prod(w.pool_shape)) * (2 if w.dtype == "bf16" else 4)
+        nsets = int(min(16, max(2, -(-(1 << 30) // pool))))
+        sets = []
+        for _ in range(nsets):
+            dw = harness.DeviceWorkload(w, "cuda")
+            dw.load_history()
+            dw.slot_mapping()
+            dw.store()
+            sets.append(dw)
+        torch.cuda.synchronize()
+
+        def all_sets():
+            for dw in sets:
+                dw.attention()
+
+        us = _graph_us(all_sets, max(10, args.steps // 10)) / nsets
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"{w.name}: pa_decode {us:.1f} us, {gbs:.1f} GB/s over {nsets} buffer sets")
+        res[w.name] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
+                       "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                       "buffer_sets": nsets}
+        del sets
+        torch.cuda.empty_cache()
+    res["timing"] = "HIP graph of one pa_decode per buffer set, replayed between two events"
+    return res
+
+
 def _graph_us(fn, reps, rounds=5):
     """Per-call GPU time of fn() (a few launches on the current stream), by HIP graph replay."""
     import torch
@@ -473,6 +516,8 @@ def main():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-graphs", action="store_true")
     ap.add_argument("--no-f16", action="store_true")
+    ap.add_argument("--no-other-decode", action="store_true",
+                    help="skip the Qwen2.5-0.5B and skewed long-context decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with 3 x 1 GiB device copies (counter calibration runs)")
     ap.add_argument("--partition", type=int, default=0,
@@ -554,6 +599,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         extra["prefill"] = time_prefill(args)
+        torch.cuda.empty_cache()
+    if not args.no_other_decode:
+        extra["other_decode"] = time_other_decode(args)
         torch.cuda.empty_cache()
     if not args.no_mixed:
         extra["mixed"] = time_mixed(args)

@@ -122,8 +122,8 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel
 // ---------------------------------------------------------------------------
 // Merges: one workgroup per (query head, sequence), one thread per element.
 
-template <int ET>
-__global__ __launch_bounds__(128) void merge_kernel(
+template <int ET, int W>
+__global__ __launch_bounds__(64 * W) void merge_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const int32_t* __restrict__ context_lens, int HQ, int D,
     int NP, int part_size) {
@@ -133,21 +133,11 @@ __global__ __launch_bounds__(128) void merge_kernel(
   const int L = context_lens[b];
   int n = L > 0 ? (L + part_size - 1) / part_size : 0;
   n = min(n, NP);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    if (n == 0) {
-      E::store(out, bh * D + d, 0.0f);
-      continue;
-    }
-    float M = -INFINITY;
-    for (int p = 0; p < n; ++p) M = fmaxf(M, ws_m[bh * NP + p]);
-    float A = 0.0f, Lt = 0.0f;
-    for (int p = 0; p < n; ++p) {
-      const float f = fast_exp2((ws_m[bh * NP + p] - M) * kLog2e);
-      A = fmaf(f, ws_acc[(bh * NP + p) * D + d], A);
-      Lt = fmaf(f, ws_l[bh * NP + p], Lt);
-    }
-    E::store(out, bh * D + d, A / Lt);
+  if (n == 0) {
+    for (int d = threadIdx.x; d < D; d += blockDim.x) E::store(out, bh * D + d, 0.0f);
+    return;
   }
+  merge_states<ET, W>(out, bh * D, ws_acc, ws_m, ws_l, n, D, [&](int k) { return bh * NP + k; });
 }
 
 // ---------------------------------------------------------------------------
@@ -213,14 +203,24 @@ static int32_t resolve_max_ctx(int32_t max_ctx, int32_t maxb, int32_t bs) {
 static int launch_merge(void* out, const DecodePlan& pl, const WsPtrs& w,
                         const int32_t* context_lens, int32_t B, int32_t HQ, int32_t D,
                         pa_dtype dtype, hipStream_t s) {
-  dim3 grid(HQ, B), block(D <= 128 ? D : 128);
-#define PA_MERGE(ET)                                                                          \
-  if (pl.mode == DecodePlan::kBalanced)                                                       \
-    hipLaunchKernelGGL((merge_balanced_kernel<ET, false>), grid, block, 0, s, out, w.acc, w.m, \
-                       w.l, w.cuc, nullptr, 0, B, HQ, D, pl.Wt);                              \
-  else                                                                                        \
-    hipLaunchKernelGGL(merge_kernel<ET>, grid, block, 0, s, out, w.acc, w.m, w.l,             \
+  // Pieces per output row: at most one more than the slices per sequence (balanced), or
+  // the partitions of the longest sequence (fixed).
+  const int64_t pieces = pl.mode == DecodePlan::kBalanced ? (pl.Wt + B - 1) / B + 1 : pl.NP;
+  const int W = merge_waves(pieces);
+  const dim3 grid(HQ, B), block(64 * W);
+#define PA_MERGE_W(ET, WV)                                                                       \
+  if (pl.mode == DecodePlan::kBalanced)                                                          \
+    hipLaunchKernelGGL((merge_balanced_kernel<ET, false, WV>), grid, block, 0, s, out, w.acc,    \
+                       w.m, w.l, w.cuc, nullptr, 0, B, HQ, D, pl.Wt);                            \
+  else                                                                                           \
+    hipLaunchKernelGGL((merge_kernel<ET, WV>), grid, block, 0, s, out, w.acc, w.m, w.l,          \
                        context_lens, HQ, D, pl.NP, pl.P);
+#define PA_MERGE(ET)            \
+  if (W == 1) {                 \
+    PA_MERGE_W(ET, 1)           \
+  } else {                      \
+    PA_MERGE_W(ET, kMergeWaves) \
+  }
   if (dtype == PA_BF16) {
     PA_MERGE(PA_BF16)
   } else if (dtype == PA_F16) {
@@ -229,6 +229,7 @@ static int launch_merge(void* out, const DecodePlan& pl, const WsPtrs& w,
     PA_MERGE(PA_F32)
   }
 #undef PA_MERGE
+#undef PA_MERGE_W
   return check_launch("decode merge");
 }
 

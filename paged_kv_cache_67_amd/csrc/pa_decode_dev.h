@@ -483,13 +483,108 @@ __device__ __forceinline__ void decode_balanced_body(
 }
 
 
+// Merge workgroups: one wave, or kMergeWaves waves for rows with many pieces; each wave
+// keeps kMergeUnroll pieces' loads in flight.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeUnroll = 8;
+// Waves per merge workgroup for a given mean number of pieces per row.
+inline int merge_waves(int64_t pieces_per_row) { return pieces_per_row >= 16 ? kMergeWaves : 1; }
+
+// Combines n partial states (m, l, acc[D]) of one output row into out[row .. row + D):
+// out = sum_k e^(m_k - M) acc_k / sum_k e^(m_k - M) l_k with M = max_k m_k (m in natural-log
+// units, the rescaling identity of the online softmax).  Piece k's m and l sit at ws_m /
+// ws_l[idx(k)] and its acc at ws_acc[idx(k) * D].  Wave w takes pieces w, w + W, w + 2W, ...,
+// kMergeUnroll at a time with all their loads issued together (pieces past n read piece
+// n - 1 and count zero), keeping a running (M, L, A) that is rescaled when M grows; with
+// W > 1 the wave states are combined through LDS.  Lane l holds d = l and, for D = 128,
+// d = l + 64.  Must be called by all 64 W threads of the workgroup.
+template <int ET, int W, typename Idx>
+__device__ __forceinline__ void merge_states(void* __restrict__ out, int64_t row,
+                                             const float* __restrict__ ws_acc,
+                                             const float* __restrict__ ws_m,
+                                             const float* __restrict__ ws_l, int n, int D,
+                                             Idx idx) {
+  using E = Elem<ET>;
+  constexpr int U = kMergeUnroll;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool two = D > 64;
+  constexpr float kFloor = -1.0e30f;  // finite: e^(kFloor - M) is 0, never NaN
+  float M = kFloor, L = 0.0f, A0 = 0.0f, A1 = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += U * W) {
+    float m[U], l[U], a0[U], a1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k0 + w + W * u;
+      const bool ok = kk < n;
+      const int64_t s = idx(min(kk, n - 1));
+      const float mv = ws_m[s], lv = ws_l[s], av0 = ws_acc[s * D + lane];
+      const float av1 = two ? ws_acc[s * D + 64 + lane] : 0.0f;
+      m[u] = ok ? mv : kFloor;
+      l[u] = ok ? lv : 0.0f;
+      a0[u] = ok ? av0 : 0.0f;
+      a1[u] = ok ? av1 : 0.0f;
+    }
+    float mn = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, m[u]);
+    const float c = fast_exp2((M - mn) * kLog2e);
+    L *= c;
+    A0 *= c;
+    A1 *= c;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = fast_exp2((m[u] - mn) * kLog2e);
+      L = fmaf(f, l[u], L);
+      A0 = fmaf(f, a0[u], A0);
+      A1 = fmaf(f, a1[u], A1);
+    }
+    M = mn;
+  }
+  if constexpr (W == 1) {
+    const float inv = 1.0f / L;
+    E::store(out, row + lane, A0 * inv);
+    if (two) E::store(out, row + 64 + lane, A1 * inv);
+  } else {
+    __shared__ float sM[W], sL[W];
+    __shared__ float sA[W][128];
+    if (lane == 0) {
+      sM[w] = M;
+      sL[w] = L;
+    }
+    sA[w][lane] = A0;
+    if (two) sA[w][64 + lane] = A1;
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = sM[0];
+#pragma unroll
+    for (int j = 1; j < W; ++j) Mt = fmaxf(Mt, sM[j]);
+    float f[W], Lt = 0.0f;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      f[j] = fast_exp2((sM[j] - Mt) * kLog2e);
+      Lt = fmaf(f[j], sL[j], Lt);
+    }
+    const float inv = 1.0f / Lt;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1 && !two) break;
+      const int d = lane + 64 * half;
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < W; ++j) a = fmaf(f[j], sA[j][d], a);
+      E::store(out, row + d, a * inv);
+    }
+  }
+}
+
+
 // Balanced split: sequence b spans slices w0 = cb / Cw .. w1 = (ce - 1) / Cw.
 // With w0 == w1 the decode pass already wrote the row; otherwise its pieces
 // are slice w0's tail state and slices w0+1 .. w1's head states.  VARLEN: only
 // the one-query sequences of a varlen batch are decode rows (row cu_q[b]); the
 // others belong to the prefill side and are left alone.
-template <int ET, bool VARLEN>
-__global__ __launch_bounds__(128) void merge_balanced_kernel(
+template <int ET, bool VARLEN, int W>
+__global__ __launch_bounds__(64 * W) void merge_balanced_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const int32_t* __restrict__ ws_cuc,
     const int32_t* __restrict__ cu_q, int total_q, int B, int HQ, int D, int Wt) {
@@ -510,21 +605,11 @@ __global__ __launch_bounds__(128) void merge_balanced_kernel(
   const int Cw = (NC + Wt - 1) / Wt;
   const int w0 = cb / Cw, w1 = (ce - 1) / Cw;
   if (w0 == w1) return;
-  const int64_t base = (int64_t)h * Wt * 2;
-  float M = ws_m[base + w0 * 2 + kTailSlot];
-  for (int w = w0 + 1; w <= w1; ++w) M = fmaxf(M, ws_m[base + w * 2 + kHeadSlot]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    int64_t s = base + w0 * 2 + kTailSlot;
-    float f = fast_exp2((ws_m[s] - M) * kLog2e);
-    float A = f * ws_acc[s * D + d], Lt = f * ws_l[s];
-    for (int w = w0 + 1; w <= w1; ++w) {
-      s = base + w * 2 + kHeadSlot;
-      f = fast_exp2((ws_m[s] - M) * kLog2e);
-      A = fmaf(f, ws_acc[s * D + d], A);
-      Lt = fmaf(f, ws_l[s], Lt);
-    }
-    E::store(out, row + d, A / Lt);
-  }
+  // Piece 0 is the tail slot of slice w0, piece k >= 1 the head slot of slice w0 + k.
+  const int64_t base = (int64_t)h * Wt * 2 + (int64_t)w0 * 2;
+  merge_states<ET, W>(out, row, ws_acc, ws_m, ws_l, w1 - w0 + 1, D, [&](int k) {
+    return base + 2 * k + (k == 0 ? kTailSlot : kHeadSlot);
+  });
 }
 
 

@@ -223,13 +223,20 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
                      w.cuc, head_waves, pl.Wt);
   int st = check_launch(fn);
   if (st) return st;
-  if (dtype == PA_F16)
-    hipLaunchKernelGGL((merge_balanced_kernel<PA_F16, true>), dim3(num_q_heads, num_seqs),
-                       dim3(head_dim), 0, s, out, w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q,
-                       num_seqs, num_q_heads, head_dim, pl.Wt);
-  else
-    hipLaunchKernelGGL((merge_balanced_kernel<PA_BF16, true>), dim3(num_q_heads, num_seqs),
-                       dim3(head_dim), 0, s, out, w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q,
-                       num_seqs, num_q_heads, head_dim, pl.Wt);
+  // Pieces per decode row: at most one more than the slices per sequence.
+  const int W = merge_waves((pl.Wt + num_seqs - 1) / num_seqs + 1);
+  const dim3 mgrid(num_q_heads, num_seqs);
+#define PA_MIXED_MERGE(ET, WV)                                                              \
+  hipLaunchKernelGGL((merge_balanced_kernel<ET, true, WV>), mgrid, dim3(64 * WV), 0, s, out, \
+                     w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q, num_seqs, num_q_heads,  \
+                     head_dim, pl.Wt)
+  if (dtype == PA_F16) {
+    if (W == 1) PA_MIXED_MERGE(PA_F16, 1);
+    else PA_MIXED_MERGE(PA_F16, kMergeWaves);
+  } else {
+    if (W == 1) PA_MIXED_MERGE(PA_BF16, 1);
+    else PA_MIXED_MERGE(PA_BF16, kMergeWaves);
+  }
+#undef PA_MIXED_MERGE
   return check_launch("pa_attention_mixed merge");
 }
