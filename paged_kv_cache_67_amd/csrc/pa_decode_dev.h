@@ -92,9 +92,10 @@ struct Elem<PA_F32> {
 #endif
 
 // Load slots per chunk: wide GQA tiles hold more q / state registers, so they
-// take smaller chunks to stay clear of spills.
+// take smaller chunks to stay clear of spills and keep two waves per SIMD (a
+// tile of 8 heads: one slot; of 7 heads: two, which still fit and run faster).
 __host__ __device__ constexpr int loads_per_chunk(int G) {
-  return G > 6 ? 1 : (G > 4 ? (PA_DECODE_LOADS > 2 ? PA_DECODE_LOADS / 2 : 1) : PA_DECODE_LOADS);
+  return G > 7 ? 1 : (G > 6 ? 2 : (G > 4 ? (PA_DECODE_LOADS > 2 ? PA_DECODE_LOADS / 2 : 1) : PA_DECODE_LOADS));
 }
 // Head waves per workgroup: 8, or 4 for the widest tiles (a wave may then use
 // up to 512 VGPRs).
