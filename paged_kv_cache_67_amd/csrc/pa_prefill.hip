@@ -10,12 +10,13 @@
 //   grid = (query tile, kv head, sequence), 8 waves (two per SIMD, so one wave's softmax
 //   and LDS traffic overlap the other's matrix work).  A workgroup owns 128 query rows: the
 //   128/G positions of its tile times the G query heads of one GQA group, so each K/V tile
-//   gathered through the block table serves every head that reads it; each wave owns 16
-//   rows.  Workgroups are renumbered so the query tiles of one (sequence, kv head) run on
-//   one XCD and share its L2.
-//   Keys go in tiles of 64 through two LDS buffers and two register sets: a tile's global
-//   loads are issued two iterations before its LDS store, one barrier per tile.  Block ids
-//   come from an LDS copy of the block table, never from global memory inside the loop.
+//   gathered through the block table serves every head that reads it; each wave owns 32
+//   rows and one half of every key tile.  Workgroups are renumbered so the query tiles of
+//   one (sequence, kv head) run on one XCD and share its L2.
+//   Keys go in tiles of 128, loaded global -> LDS directly (no register staging) into two
+//   K and two V buffers: a step issues the next tiles' loads first and waits for them only
+//   at its end, one barrier per step.  Block ids come from an LDS copy of the block table,
+//   never from global memory inside the loop.
 //   Both K and V sit in LDS in their natural [key][d] layout.  Each wave computes
 //   S^T = K Q^T (16 keys x 16 queries per v_mfma_f32_16x16x32_bf16), so every lane holds
 //   scores of a single query: the online softmax needs two cross-lane exchanges per tile

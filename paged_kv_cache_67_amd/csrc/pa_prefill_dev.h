@@ -14,7 +14,7 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte register chunk
 
 constexpr int kPrefillRows = 128;     // query rows (position x head) per workgroup
-constexpr int kPrefillKeys = 64;      // keys per tile
+constexpr int kPrefillKeys = 128;     // keys per tile
 constexpr int kPrefillThreads = 512;  // 8 waves: 4 row groups x 2 key halves
 constexpr int kBtCache = 2048;        // block-table entries of one sequence kept in LDS
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
@@ -48,6 +48,21 @@ struct Mfma<PA_F16> {
   __device__ static uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 };
 
+// 16 bytes per lane from global memory straight into LDS, lane i at byte lds + 16 i
+// (global_load_lds_dwordx4, LDS address in M0, the same for the whole wave).  Written as
+// inline assembly so that the compiler does not hold every later LDS read of the tile
+// buffers until all of these loads have landed: the caller waits for them itself
+// (s_waitcnt vmcnt) before the barrier that publishes a tile.  One wait state separates
+// the M0 write from the load.  The compiler reserves M0 and sets it right before each
+// instruction that reads it; no code in these kernels does, so the clobber is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Max over the four lanes l, l^16, l^32, l^48 (the lanes that hold one query's scores), on
 // gfx950's lane-swap instructions instead of an LDS round trip.
 __device__ __forceinline__ float max_over_groups(float x) {
@@ -61,21 +76,26 @@ __device__ __forceinline__ float max_over_groups(float x) {
 //   A[m][k]: lane holds m = lane % 16, k = (group, i = 0..7); B[k][n]: n = lane % 16;
 //   C/D[m][n]: lane holds m = 4 * group + i (i = 0..3), n = lane % 16.
 // Wave w owns 32 query rows, 32*(w%4) + 16*qg + lane%16 for query groups qg = 0, 1, and
-// the 32 keys 32*(w/4) + 0..31 of every 64-key tile (its key half).  Both query groups
-// share every K and V operand read.  S^T = K Q^T per 16-key block kb: lane holds the
-// scores of its query for keys 16kb + 4*group + i of the half.  For O^T += V^T P^T over
-// the half's 32 keys, the MFMA k index (group, i) stands for key 16*(i/4) + 4*group + i%4
-// on both operands: P comes straight from blocks kb = 0, 1, V^T from two transposing LDS
-// reads.  The row sums l come from one more MFMA with an all-ones A operand, so they are
-// summed from the same bf16 probabilities as the numerator.  The two key halves of a row
-// keep separate (m, l, O) and are merged through LDS at the end.
+// the 64 keys 64*(w/4) + 0..63 of every 128-key tile (its key half).  Both query groups
+// share every K and V operand read.  S^T = K Q^T per 16-key block kb = 0..3: lane holds
+// the scores of its query for keys 16kb + 4*group + i of the half.  For O^T += V^T P^T
+// over 32 keys at a time (ks = 0, 1), the MFMA k index (group, i) stands for key
+// 32ks + 16*(i/4) + 4*group + i%4 on both operands: P comes straight from blocks 2ks and
+// 2ks + 1, V^T from two transposing LDS reads.  The row sums l come from one more MFMA
+// with an all-ones A operand, so they are summed from the same bf16 probabilities as the
+// numerator.  The two key halves of a row keep separate (m, l, O) and are merged through
+// LDS at the end.
 //
-// Pipeline: iteration t holds S_t in registers, computes S_{t+1} from K tile t+1 while it
-// exponentiates S_t, then accumulates V tile t.  K therefore runs one tile ahead of V in
-// LDS and in the loads: at the end of iteration t the register set R (B for even t, A for
-// odd) holds K_{t+2} and V_{t+1}, is written to LDS, and is refilled with K_{t+4} and
-// V_{t+3}.  WIDE (block_size >= 64): every tile lies inside one block, so a tile's address
-// is a scalar base plus a per-lane offset that does not change from tile to tile.
+// LDS: two K and two V tile buffers of 128 rows x D, unpadded; the 16-byte chunks of row r
+// are permuted by XOR with swz(r), so that the 16 rows one K operand read touches (16
+// lanes, one chunk each) and the 8 rows of a transposing read's half wave (two chunks
+// each) fall on distinct banks.
+//
+// Pipeline: step t holds S_t in registers; it computes S_{t+1} from K tile t+1 while it
+// exponentiates S_t, then accumulates V tile t.  At its start it issues K_{t+2} and
+// V_{t+1} straight into the two buffers step t - 1 finished reading, and it ends with a
+// wait for them and one barrier.  WIDE (block_size >= 128): every tile lies inside one
+// block, so a tile's address is a scalar base plus a per-lane offset.
 // The body of one workgroup item: query tile qt of sequence b for KV head g.  MIXED: the
 // batch also holds decode rows (sequences with one query), which the decode side of the
 // launch handles; such a sequence is skipped here.
@@ -91,14 +111,17 @@ __device__ __forceinline__ void prefill_body(
   constexpr int BM = kPrefillRows / G;  // positions per workgroup
   constexpr int BN = kPrefillKeys;
   constexpr int NT = kPrefillThreads;
-  constexpr int P = D + 16;   // K and V row pitch (bf16); conflict-free for both LDS reads
+  constexpr int BNH = BN / 2;  // keys per key half
+  constexpr int KB = BNH / 16;  // 16-key blocks of S^T per key half
+  constexpr int KS = BNH / 32;  // 32-key steps of O^T += V^T P^T per key half
   constexpr int DS = D / 32;  // 32-wide d steps of S^T
   constexpr int DB = D / 16;  // 16-wide d blocks of O^T
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int LPT = BN * CPR / NT;  // 16-byte loads per thread per tile (K and V each)
-  // K tiles in buffers 0, 1 and V tiles in 2, 3; after the loop the same memory carries
-  // the key-half partial results (4 x 2 x 32 x 64 floats of O, then m and l).
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[4][BN * P];
+  // K tiles in buffers 0, 1 and V tiles in 2, 3: unpadded rows of D elements whose 16-byte
+  // chunks are XOR-swizzled per row.  After the loop the same memory carries the key-half
+  // partial results (4 x 2 x 32 x 64 floats of O, then m and l).
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[4][BN * D];
   static_assert(sizeof(sKV) >= (4 * 2 * (4 * DB + 2) * 64) * sizeof(float), "merge area");
   __shared__ int s_bt[kBtCache];
   static_assert(kBtCache % NT == 0, "block-table window split over the threads");
@@ -201,67 +224,63 @@ __device__ __forceinline__ void prefill_body(
     return s_bt[max(min(jb - btb, min(nblk - btb, kBtCache) - 1), 0)];
   };
 
-  // Thread tid moves 16-byte chunks c = tid + NT*i of a tile: key row c / CPR, d chunk c % CPR.
+  auto swz = [](int r) __attribute__((always_inline)) {
+    return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  };
+  // Tile loads go straight into LDS: load i of wave w fills chunk positions 64 (w + 8 i) +
+  // lane of the tile, i.e. row trow[i], position p, which holds global chunk p ^ swz(row).
   int trow[LPT], tcol[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    trow[i] = (tid + NT * i) / CPR;
-    tcol[i] = g * D + ((tid + NT * i) % CPR) * 8;
+    const int qp = 64 * (w + 8 * i) + lane;
+    trow[i] = qp / CPR;
+    tcol[i] = g * D + (((qp % CPR) ^ swz(trow[i])) * 8);
   }
-  // A tile start of nk or more (past the last tile) loads key nk - 1 and is never used.
-  int64_t off[LPT];  // general path: element offsets of the K tile loaded last
-  auto tile_offsets = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int j = min(kt + trow[i], nk - 1);
-      off[i] = (int64_t)lookup(j >> bs_log2) * ((int64_t)HKVD << bs_log2) +
-               (int)((j & bs_mask) * HKVD + tcol[i]);
-    }
-  };
-  auto load_wide = [&](const uint16_t* src, int kt, u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
-    const int ktc = min(kt, (ntiles - 1) * BN);
-    const int blk = __builtin_amdgcn_readfirstlane(lookup(ktc >> bs_log2));
-    const uint16_t* base = src + (((int64_t)blk << bs_log2) + (ktc & bs_mask)) * HKVD;
-    const int lim = nk - 1 - ktc;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i)
-      r[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) +
-                                               (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])));
-  };
-  auto load_k = [&](int kt, u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
-    cover(kt);
+  // A tile past the last one loads the last tile's keys (clamped to key nk - 1) and is
+  // never read.
+  auto issue = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
     if constexpr (WIDE) {
-      load_wide(kc, kt, r);
-    } else {
-      tile_offsets(kt);
+      const int ktc = min(kt, (ntiles - 1) * BN);
+      const int blk = __builtin_amdgcn_readfirstlane(lookup(ktc >> bs_log2));
+      const uint16_t* base = src + (((int64_t)blk << bs_log2) + (ktc & bs_mask)) * HKVD;
+      const int lim = nk - 1 - ktc;
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(kc + off[i]);
-    }
-  };
-  // V tile kt always follows the K load of the same tile (no window move in between); the
-  // general path reuses that load's offsets.
-  auto load_v = [&](int kt, u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
-    if constexpr (WIDE) {
-      load_wide(vc, kt, r);
+      for (int i = 0; i < LPT; ++i)
+        load_to_lds(reinterpret_cast<const char*>(base) + (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])),
+                    (uint32_t)(uintptr_t)(dst + 512 * (w + 8 * i)));
     } else {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) r[i] = *reinterpret_cast<const u32x4_t*>(vc + off[i]);
+      for (int i = 0; i < LPT; ++i) {
+        const int j = min(kt + trow[i], nk - 1);
+        const int64_t off = (int64_t)lookup(j >> bs_log2) * ((int64_t)HKVD << bs_log2) +
+                            (int)((j & bs_mask) * HKVD + tcol[i]);
+        load_to_lds(src + off, (uint32_t)(uintptr_t)(dst + 512 * (w + 8 * i)));
+      }
     }
   };
-  auto store = [&](uint16_t* dst, const u32x4_t (&r)[LPT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i)
-      *reinterpret_cast<u32x4_t*>(dst + trow[i] * P + (tcol[i] - g * D)) = r[i];
+  auto issue_k = [&](int t) __attribute__((always_inline)) {
+    cover(t * BN);
+    issue(kc, t * BN, sKV[t & 1]);
   };
-  const int krow = 32 * kh + qc;  // K operand row of block kb = 0 in this wave's key half
-  auto scores = [&](const uint16_t* K, f32x4_t (&s)[2][2]) __attribute__((always_inline)) {
+  auto issue_v = [&](int t) __attribute__((always_inline)) { issue(vc, t * BN, sKV[2 + (t & 1)]); };
+  // Barrier without a memory fence: first wait for every tile load (the compiler does not
+  // count them) and LDS access of this wave.
+  auto bar_tiles = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  const int krow = BNH * kh + qc;  // K operand row of block kb = 0 in this wave's key half
+  auto scores = [&](const uint16_t* K, f32x4_t (&s)[2][KB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       s[0][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       s[1][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const int r = krow + 16 * kb;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const v8 a = *reinterpret_cast<const v8*>(&K[(krow + 16 * kb) * P + 32 * ds + 8 * grp]);
+        const v8 a = *reinterpret_cast<const v8*>(&K[r * D + (((4 * ds + grp) ^ swz(r)) * 8)]);
         s[0][kb] = M::mma(a, qreg[0][ds], s[0][kb]);
         s[1][kb] = M::mma(a, qreg[1][ds], s[1][kb]);
       }
@@ -283,36 +302,42 @@ __device__ __forceinline__ void prefill_body(
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = M::cvt(1.0f);
 
-  // Transposing read: lane p = a + 4t of group grp addresses key 4*grp + t (+16 for the
-  // second half) of the key half at d column 4a (+16db); lane 4a + c then holds
-  // d = 16db + 4a + c.
-  const int tr_off = (32 * kh + 4 * grp + ((lane & 15) >> 2)) * P + 4 * (lane & 3);
+  // Transposing read: lane p = a + 4t of group grp addresses key 32ks + 4*grp + t (+16 for
+  // the second read) of the key half at d column 4a (+16db); lane 4a + c then holds
+  // d = 16db + 4a + c.  Column 16db + 4a lies in chunk 2db + a/2, at byte 8 (a & 1); rows
+  // 16 apart share the swizzle.
+  const int tr_row = BNH * kh + 4 * grp + ((lane & 15) >> 2);
+  int tr_off[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    tr_off[db] = tr_row * D + (((2 * db + ((lane & 3) >> 1)) ^ swz(tr_row)) * 8) + 4 * (lane & 1);
 
-  u32x4_t rkA[LPT], rvA[LPT], rkB[LPT], rvB[LPT];
-  f32x4_t sc[2][2];  // scores of the tile being reduced
-  // Every path issues the same loads in the same order, so the compiler's wait counts stay
-  // exact: writing one register set to LDS waits for that set only.
-  auto step = [&](int t, u32x4_t (&rk)[LPT], u32x4_t (&rv)[LPT]) __attribute__((always_inline)) {
+  f32x4_t sc[2][KB];  // scores of the tile being reduced
+  auto step = [&](int t) __attribute__((always_inline)) {
     const int kt = t * BN;
+    // V_{t+1} and K_{t+2} into the buffers step t - 1 finished reading.
+    issue_v(t + 1);
+    issue_k(t + 2);
     if (kt + BN > nk_min) {
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = kt + 32 * kh + 16 * kb + 4 * grp + i;
+            const int key = kt + BNH * kh + 16 * kb + 4 * grp + i;
             sc[qg][kb][i] = key < row_nk[qg] ? sc[qg][kb][i] : -INFINITY;
           }
     }
-    // The running max moves only when some score of the row exceeds it by more than
-    // kLazyRescale (log2 units): a per-lane test against thr = (m + kLazyRescale) / scale
-    // decides that, and only then is the row max taken across the row's lanes.
     float lmx[2];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg)
-      lmx[qg] = fmaxf(fmaxf(fmaxf(sc[qg][0][0], sc[qg][0][1]), fmaxf(sc[qg][0][2], sc[qg][0][3])),
-                      fmaxf(fmaxf(sc[qg][1][0], sc[qg][1][1]), fmaxf(sc[qg][1][2], sc[qg][1][3])));
+    for (int qg = 0; qg < 2; ++qg) {
+      lmx[qg] = sc[qg][0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lmx[qg] = fmaxf(lmx[qg], sc[qg][kb][i]);
+    }
     if (__builtin_amdgcn_ballot_w64(lmx[0] > thr[0] || lmx[1] > thr[1])) {
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
@@ -327,74 +352,98 @@ __device__ __forceinline__ void prefill_body(
       }
     }
 
-    f32x4_t sn[2][2];
-    scores(sKV[(t + 1) & 1], sn);
-    v8 pb[2];
+    // S_{t+1} = K_{t+1} Q^T interleaved with P_t = exp2(S_t c - m): KB * DS groups of one K
+    // operand read two groups ahead, two MFMAs and EPG exponentials per lane (32 in all).
+    constexpr int NG = KB * DS;
+    constexpr int EPG = 2 * 4 * KB / NG;  // exponentials per group
+    static_assert(EPG % 2 == 0 && EPG * NG == 8 * KB, "pairs of exponentials per group");
+    const uint16_t* Kn = sKV[(t + 1) & 1];
+    auto read_k = [&](int i) __attribute__((always_inline)) {
+      const int r = krow + 16 * (i / DS);
+      return *reinterpret_cast<const v8*>(&Kn[r * D + (((4 * (i % DS) + grp) ^ swz(r)) * 8)]);
+    };
+    f32x4_t sn[2][KB];
+    v8 pb[2][KS];
+    v8 kr[3];
+    __builtin_amdgcn_sched_barrier(0);
+    kr[0] = read_k(0);
+    kr[1] = read_k(1);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (i + 2 < NG) kr[(i + 2) % 3] = read_k(i + 2);
+      const int kb = i / DS, ds = i % DS;
+      if (ds == 0) {
+        sn[0][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        sn[1][kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      sn[0][kb] = M::mma(kr[i % 3], qreg[0][ds], sn[0][kb]);
+      sn[1][kb] = M::mma(kr[i % 3], qreg[1][ds], sn[1][kb]);
+      // elements EPG i .. EPG i + EPG - 1 of this lane's 32 probabilities: element j is
+      // query group j / 16, key block (j / 4) % 4, entry j % 4
+#pragma unroll
+      for (int j = EPG * i; j < EPG * i + EPG; ++j) {
+        const int qg = j / 16, ekb = (j / 4) % 4, ii = j % 4;
+        pb[qg][ekb / 2][4 * (ekb % 2) + ii] = M::cvt(fast_exp2(fmaf(sc[qg][ekb][ii], scale_log2, -m[qg])));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // O^T += V^T P^T, the transposing reads of d block db + 1 issued before the MFMAs of
+    // block db (and the row-sum MFMAs covering the first reads).
+    const uint16_t* V = sKV[2 + (t & 1)];
+    v4i16_t vr[2][2 * KS];
+    auto read_v = [&](int db, v4i16_t (&r)[2 * KS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint16_t* Vk = V + tr_off[db] + 32 * ks * D;
+        r[2 * ks] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4i16_t __attribute__((address_space(3)))*)(Vk));
+        r[2 * ks + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4i16_t __attribute__((address_space(3)))*)(Vk + 16 * D));
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    read_v(0, vr[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      lsum[0] = M::mma(ones, pb[0][ks], lsum[0]);
+      lsum[1] = M::mma(ones, pb[1][ks], lsum[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (db + 1 < DB) read_v(db + 1, vr[(db + 1) & 1]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const v8 a = __builtin_bit_cast(
+            v8, __builtin_shufflevector(vr[db & 1][2 * ks], vr[db & 1][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[0][db] = M::mma(a, pb[0][ks], o[0][db]);
+        o[1][db] = M::mma(a, pb[1][ks], o[1][db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // V_{t+1} and K_{t+2} must have landed before the next step.
+    bar_tiles();
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[qg][i] = M::cvt(fast_exp2(fmaf(sc[qg][0][i], scale_log2, -m[qg])));
-        pb[qg][4 + i] = M::cvt(fast_exp2(fmaf(sc[qg][1][i], scale_log2, -m[qg])));
-      }
-
-    const uint16_t* V = sKV[2 + (t & 1)] + tr_off;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (v4i16_t __attribute__((address_space(3)))*)(V + 16 * db));
-      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (v4i16_t __attribute__((address_space(3)))*)(V + 16 * db + 16 * P));
-      const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[0][db] = M::mma(a, pb[0], o[0][db]);
-      o[1][db] = M::mma(a, pb[1], o[1][db]);
-    }
-    lsum[0] = M::mma(ones, pb[0], lsum[0]);
-    lsum[1] = M::mma(ones, pb[1], lsum[1]);
-
-    // K_{t+2} into the K buffer read last iteration, V_{t+1} into the V buffer read last
-    // iteration (stale tiles past the end are written but never read).
-    store(sKV[t & 1], rk);
-    store(sKV[2 + ((t + 1) & 1)], rv);
-    load_v(t + 3 < ntiles ? kt + 3 * BN : nk, rv);
-    load_k(t + 4 < ntiles ? kt + 4 * BN : nk, rk);
-    __syncthreads();
-#pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-      sc[qg][0] = sn[qg][0];
-      sc[qg][1] = sn[qg][1];
-    }
+      for (int kb = 0; kb < KB; ++kb) sc[qg][kb] = sn[qg][kb];
   };
 
   if (ntiles > 0) {
-    // Prologue: K_0, K_1, V_0 into LDS; B = (K_2, V_1), A = (K_3, V_2) in flight.
-    load_k(0, rkA);
-    load_v(0, rvA);
-    load_k(ntiles > 1 ? BN : nk, rkB);
-    load_v(ntiles > 1 ? BN : nk, rvB);
-    store(sKV[0], rkA);
-    store(sKV[2], rvA);
-    store(sKV[1], rkB);
-    load_k(ntiles > 2 ? 2 * BN : nk, rkB);
-    load_v(ntiles > 2 ? 2 * BN : nk, rvA);
-    load_k(ntiles > 3 ? 3 * BN : nk, rkA);
-    // Settle the Q loads here, behind the tile loads issued after them: otherwise the wait
-    // for them lands in the loop header as a full drain of every load in flight.
+    issue_k(0);
+    issue_v(0);
+    issue_k(1);
+    // Settle the Q loads here: the compiler does not count the tile loads, so this wait
+    // also covers K_0, V_0 and K_1.
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+v"(qreg[qg][ds]));
-    __syncthreads();
+    bar_tiles();
     scores(sKV[0], sc);
-    __syncthreads();  // iteration 0 overwrites buffer 0
-    // Two steps per trip and no exit between them: an exit there lets the compiler sink
-    // the first step's loads past it, and the wait counts at the loop header turn into
-    // full drains.  With an odd tile count the last step runs past the end, where every
-    // key is masked and it adds nothing.
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, rkB, rvB);
-      step(t + 1, rkA, rvA);
-    }
+    bar_tiles();  // step 0 refills buffer 0
+    for (int t = 0; t < ntiles; ++t) step(t);
   }
 
   // Merge the key halves: waves 4..7 publish (m, l, O) of their rows, waves 0..3 combine.
