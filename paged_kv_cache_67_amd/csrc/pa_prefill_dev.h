@@ -229,12 +229,17 @@ __device__ __forceinline__ void prefill_body(
   };
   // Tile loads go straight into LDS: load i of wave w fills chunk positions 64 (w + 8 i) +
   // lane of the tile, i.e. row trow[i], position p, which holds global chunk p ^ swz(row).
+  // The LDS destinations are wave-uniform (scalar); toff[i] is the byte offset of load i
+  // within an unclamped tile.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   int trow[LPT], tcol[LPT];
+  uint32_t toff[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int qp = 64 * (w + 8 * i) + lane;
     trow[i] = qp / CPR;
     tcol[i] = g * D + (((qp % CPR) ^ swz(trow[i])) * 8);
+    toff[i] = 2u * (uint32_t)(trow[i] * HKVD + tcol[i]);
   }
   // A tile past the last one loads the last tile's keys (clamped to key nk - 1) and is
   // never read.
@@ -244,17 +249,24 @@ __device__ __forceinline__ void prefill_body(
       const int blk = __builtin_amdgcn_readfirstlane(lookup(ktc >> bs_log2));
       const uint16_t* base = src + (((int64_t)blk << bs_log2) + (ktc & bs_mask)) * HKVD;
       const int lim = nk - 1 - ktc;
+      if (lim >= BN - 1) {  // a whole tile: no row clamps
 #pragma unroll
-      for (int i = 0; i < LPT; ++i)
-        load_to_lds(reinterpret_cast<const char*>(base) + (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])),
-                    (uint32_t)(uintptr_t)(dst + 512 * (w + 8 * i)));
+        for (int i = 0; i < LPT; ++i)
+          load_to_lds(reinterpret_cast<const char*>(base) + toff[i],
+                      (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < LPT; ++i)
+          load_to_lds(reinterpret_cast<const char*>(base) + (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])),
+                      (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int j = min(kt + trow[i], nk - 1);
         const int64_t off = (int64_t)lookup(j >> bs_log2) * ((int64_t)HKVD << bs_log2) +
                             (int)((j & bs_mask) * HKVD + tcol[i]);
-        load_to_lds(src + off, (uint32_t)(uintptr_t)(dst + 512 * (w + 8 * i)));
+        load_to_lds(src + off, (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
       }
     }
   };
