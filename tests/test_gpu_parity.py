@@ -393,6 +393,7 @@ MIXED_CASES = [
     (14, 2, 64, 16, [300, 5, 129, 2048, 7], [100, 1, 129, 1, 1]),   # group 7
     (32, 2, 128, 64, [150, 260, 3, 90], [40, 1, 1, 90]),              # group 16
     (4, 1, 64, 8, [90, 40, 1, 17000], [90, 1, 1, 1]),                 # table past the LDS window
+    (8, 4, 128, 128, [385, 129, 1, 640], [129, 1, 1, 128]),           # one key tile per block
 ]
 
 
