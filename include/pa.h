@@ -67,7 +67,8 @@ typedef enum pa_status {
   PA_ERR_ALIGN = 4,       /* a pointer or stride breaks the 16-byte alignment rule */
   PA_ERR_WORKSPACE = 5,   /* workspace smaller than pa_decode_workspace_size() */
   PA_ERR_HIP = 6,         /* the HIP runtime rejected a launch */
-  PA_ERR_CAPACITY = 7     /* block manager: not enough free blocks */
+  PA_ERR_CAPACITY = 7,    /* block manager: not enough free blocks */
+  PA_ERR_CONTRACT = 8     /* pa_check_*: device-side metadata breaks the contract */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
@@ -320,6 +321,42 @@ int pa_attention_mixed(void* out, const void* q, const void* k_cache, const void
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
                    int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                    int32_t head_dim, pa_dtype dtype, void* stream);
+
+/*
+ * Debug checks of the device-side contract stated at the top of this file.
+ * Each drains `stream`, copies the metadata to the host and checks it there:
+ * for debugging and tests, not for the hot path (it synchronises, so it
+ * cannot be captured in a graph).  A library built with -DPA_DEBUG_CHECKS
+ * runs the matching check at the start of pa_store_kv, pa_decode,
+ * pa_decode_partitions, pa_prefill_paged and pa_attention_mixed.
+ *
+ * pa_check_store_inputs: every slot_mapping entry is -1 or in
+ *   [0, num_blocks*block_size), and no slot appears twice.
+ * pa_check_decode_inputs: 0 <= context_lens[b] <= max_context_len (or
+ *   max_blocks_per_seq*block_size when max_context_len <= 0, and never
+ *   above it), and the first ceil(context_lens[b]/block_size) block ids of
+ *   row b are in [0, num_blocks).
+ * pa_check_prefill_inputs: cu_seqlens_q and cu_seqlens_k never decrease;
+ *   cu_seqlens_q lies within [0, total_q]; each sequence has at most
+ *   max_seqlen_q queries and max_seqlen_k keys, and at least as many keys as
+ *   queries; its first ceil(keys/block_size) block ids are in
+ *   [0, num_blocks).  Also covers pa_attention_mixed.
+ *
+ * Arguments mean what they mean for the matching call; pointers are DEVICE
+ * pointers.  Returns PA_OK, PA_ERR_CONTRACT with pa_last_error() naming the
+ * first violation, PA_ERR_SHAPE / PA_ERR_NULL for bad host arguments, or
+ * PA_ERR_HIP if the copy fails.
+ */
+int pa_check_store_inputs(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                          int32_t block_size, void* stream);
+int pa_check_decode_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                           int32_t num_blocks, int32_t block_size, void* stream);
+int pa_check_prefill_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_blocks, int32_t block_size,
+                            void* stream);
 
 /*
  * Host-side block manager with a chain-hash prefix cache ([KVblog] 3.3, 3.4;

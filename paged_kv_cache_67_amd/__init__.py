@@ -17,6 +17,9 @@ from ._binding import (  # noqa: F401
     lib_path,
     pa_attention_mixed,
     pa_chain_hash,
+    pa_check_decode_inputs,
+    pa_check_prefill_inputs,
+    pa_check_store_inputs,
     pa_copy_blocks,
     pa_decode,
     pa_decode_merge,

@@ -18,7 +18,8 @@ _lib = None
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-          4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY"}
+          4: "PA_ERR_ALIGN", 5: "PA_ERR_WORKSPACE", 6: "PA_ERR_HIP", 7: "PA_ERR_CAPACITY",
+          8: "PA_ERR_CONTRACT"}
 
 _i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _u64, _pi32 = C.c_uint64, C.POINTER(C.c_int32)
@@ -44,6 +45,10 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp, _sz,
                                      _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_check_store_inputs": (C.c_int, [_vp, _i32, _i32, _i32, _vp]),
+    "pa_check_decode_inputs": (C.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "pa_check_prefill_inputs": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _vp]),
     "pa_chain_hash": (_u64, [_pi32, _i32, _i32, _u64]),
     "pa_bm_create": (_vp, [_i32, _i32]),
     "pa_bm_destroy": (None, [_vp]),
@@ -238,6 +243,38 @@ def pa_attention_mixed(out, q, k_cache, v_cache, block_table, cu_seqlens_q, cu_s
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k), NB, BS,
         HQ, HKV, D, float(scale), _dtype(q), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_check_store_inputs(slot_mapping, num_blocks, block_size, stream=None):
+    """Debug check of a store's slots (synchronises): raises PAError naming the first
+    slot outside {-1} and [0, num_blocks * block_size) or the first repeated slot."""
+    _i32_vec(slot_mapping, slot_mapping.shape[0], "slot_mapping")
+    _check("pa_check_store_inputs", lib().pa_check_store_inputs(
+        _ptr(slot_mapping), slot_mapping.shape[0], num_blocks, block_size, _stream(stream)))
+
+
+def pa_check_decode_inputs(block_table, context_lens, num_blocks, block_size, max_context_len=0,
+                           stream=None):
+    """Debug check of a decode batch's lengths and block ids (synchronises)."""
+    B = block_table.shape[0]
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    _i32_vec(context_lens, B, "context_lens")
+    _check("pa_check_decode_inputs", lib().pa_check_decode_inputs(
+        _ptr(block_table), block_table.shape[1], _ptr(context_lens), B, int(max_context_len),
+        num_blocks, block_size, _stream(stream)))
+
+
+def pa_check_prefill_inputs(block_table, cu_seqlens_q, cu_seqlens_k, total_q, max_seqlen_q,
+                            max_seqlen_k, num_blocks, block_size, stream=None):
+    """Debug check of a varlen batch's offsets, lengths and block ids (synchronises)."""
+    B = block_table.shape[0]
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    _i32_vec(cu_seqlens_q, B + 1, "cu_seqlens_q")
+    _i32_vec(cu_seqlens_k, B + 1, "cu_seqlens_k")
+    _check("pa_check_prefill_inputs", lib().pa_check_prefill_inputs(
+        _ptr(block_table), block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B,
+        int(total_q), int(max_seqlen_q), int(max_seqlen_k), num_blocks, block_size,
+        _stream(stream)))
 
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):

@@ -42,6 +42,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_CAPACITY: return "not enough free blocks";
+    case PA_ERR_CONTRACT: return "device-side metadata breaks the contract";
     default: return "unknown status";
   }
 }
