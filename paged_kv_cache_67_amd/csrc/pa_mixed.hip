@@ -9,19 +9,17 @@
 // 5), so one batch can hold prompt chunks and decode rows with no per-batch
 // prefill/decode switch.
 //
-// MI355X design.  One grid of 512-thread workgroups: the first n_pf (at most
-// one per compute unit) walk the list of query tiles of the sequences with
-// Lq > 1 (MFMA prefill body), the rest run the balanced split-K decode body over
-// the sequences with Lq = 1 (each wave one (slice, KV-head tile) of the
-// flattened decode keys).  Workgroups are handed out in launch order, so decode
-// slices fill the compute units as the prefill tiles drain; no workgroup is
-// launched for a decode row's would-be prefill tile.  When the batch holds decode
-// rows, only the first half of the prefill workgroups (as many per XCD) take tiles
-// and the rest leave at once: the bandwidth-bound decode slices then run on half
-// the chip alongside the latency-bound prefill tiles instead of after them
-// (measured on 256 decode rows + 8 x 256-token chunks: 396 us against 414 us with
-// every compute unit on prefill first).  Decode rows cut by slice
-// boundaries leave partial states in the workspace; a second small launch
+// MI355X design.  One grid of 512-thread workgroups: the first ones run the
+// balanced split-K decode body over the sequences with Lq = 1 (each wave one
+// (slice, KV-head tile) of the flattened decode keys), the last n_pf (at most one
+// per compute unit) walk the list of query tiles of the sequences with Lq > 1
+// (MFMA prefill body).  Workgroups are handed out in launch order, so the
+// latency-bound prefill tiles take the compute units that the bandwidth-bound
+// decode slices free in the decode's tail, and no workgroup is launched for a
+// decode row's would-be prefill tile (measured on 256 decode rows + 8 x 256-token
+// chunks: 384 us, against 386 us as two launches, 395 us with half the compute
+// units on prefill tiles first and 414 us with all of them).  Decode rows cut by
+// slice boundaries leave partial states in the workspace; a second small launch
 // merges them.
 #include "pa_decode_plan.h"
 #include "pa_prefill_dev.h"
@@ -38,27 +36,24 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
     int num_blocks, int bs_log2, int HQ, int HKV, float scale_log2, int n_pf,
     float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
     int32_t* __restrict__ ws_cuc, int head_waves, int Wt) {
-  if ((int)blockIdx.x < n_pf) {
+  const int pf_id = (int)blockIdx.x - ((int)gridDim.x - n_pf);  // prefill workers come last
+  if (pf_id >= 0) {
     // Prefill workgroups walk a list of the batch's query tiles, built here from cu_q: a
     // sequence with Lq >= 2 has ceil(Lq / BM) tiles per KV head.  Items are numbered
     // sequence, then KV head, then tile, and handed out so that consecutive items run on
     // one XCD (tiles of one sequence and KV head read the same K/V rows through its L2).
     constexpr int BM = kPrefillRows / G;
-    // [B + 1] exclusive prefix sums of tiles per sequence, then a flag: the batch has
-    // decode rows.
+    // [B + 1] exclusive prefix sums of tiles per sequence.
     extern __shared__ int s_items[];
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
       const int seg = (B + 63) / 64;
       const int lo = min(B, lane * seg), hi = min(B, lo + seg);
       int sum = 0;
-      bool dec = false;
       for (int i = lo; i < hi; ++i) {
         const int Lq = cu_q[i + 1] - cu_q[i];
         sum += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
-        dec |= Lq == 1;
       }
-      const bool any_dec = __builtin_amdgcn_ballot_w64(dec) != 0;
       int incl = sum;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -72,16 +67,10 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
         run += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
       }
       if (lane == 63) s_items[B] = incl;
-      if (lane == 0) s_items[B + 1] = any_dec;
     }
     __syncthreads();
     const int items = HKV * lds_uniform(s_items + B);
-    // With decode rows in the batch, at most half the compute units take prefill work
-    // (the first blocks, the same number on every XCD); the others leave at once and
-    // their units run decode slices alongside.
-    const int n_use = lds_uniform(s_items + B + 1) ? min(n_pf, kNumCUs / 2) : n_pf;
-    if ((int)blockIdx.x >= n_use) return;
-    for (int j = xcd_local_id(blockIdx.x, n_use); j < items; j += n_use) {
+    for (int j = xcd_local_id(pf_id, n_pf); j < items; j += n_pf) {
       int lo = 0, hi = B;  // the sequence: largest b with HKV * s_items[b] <= j
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -96,7 +85,7 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
       __syncthreads();  // the next item reuses this item's LDS
     }
   } else {
-    const int i = blockIdx.x - n_pf;
+    const int i = blockIdx.x;
     const int item = i * (kPrefillThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     decode_balanced_body<D, ET, head_tile(G), true>(
         item / head_waves, item % head_waves, i == 0, out, ws_acc, ws_m, ws_l, ws_cuc, q, kc, vc,
