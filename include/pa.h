@@ -326,9 +326,13 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
  * Debug checks of the device-side contract stated at the top of this file.
  * Each drains `stream`, copies the metadata to the host and checks it there:
  * for debugging and tests, not for the hot path (it synchronises, so it
- * cannot be captured in a graph).  A library built with -DPA_DEBUG_CHECKS
- * runs the matching check at the start of pa_store_kv, pa_decode,
- * pa_decode_partitions, pa_prefill_paged and pa_attention_mixed.
+ * cannot be captured in a graph).  When the checks are switched on, the
+ * matching check runs at the start of pa_store_kv, pa_decode,
+ * pa_decode_partitions, pa_prefill_paged and pa_attention_mixed, which then
+ * return its status instead of launching.  They start switched on when the
+ * environment variable PA_DEBUG_CHECKS is set to anything but "0" at the
+ * first call that looks; pa_set_debug_checks(on) switches them for the whole
+ * process and returns the previous setting (0 / 1).
  *
  * pa_check_store_inputs: every slot_mapping entry is -1 or in
  *   [0, num_blocks*block_size), and no slot appears twice.
@@ -347,6 +351,7 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
  * first violation, PA_ERR_SHAPE / PA_ERR_NULL for bad host arguments, or
  * PA_ERR_HIP if the copy fails.
  */
+int pa_set_debug_checks(int on);
 int pa_check_store_inputs(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                           int32_t block_size, void* stream);
 int pa_check_decode_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,

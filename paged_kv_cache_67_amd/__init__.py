@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     pa_last_error,
     pa_mixed_workspace_size,
     pa_prefill_paged,
+    pa_set_debug_checks,
     pa_slot_mapping,
     pa_status_string,
     pa_store_kv,

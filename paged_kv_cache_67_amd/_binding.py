@@ -45,6 +45,7 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp, _sz,
                                      _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_set_debug_checks": (C.c_int, [C.c_int]),
     "pa_check_store_inputs": (C.c_int, [_vp, _i32, _i32, _i32, _vp]),
     "pa_check_decode_inputs": (C.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_check_prefill_inputs": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -243,6 +244,12 @@ def pa_attention_mixed(out, q, k_cache, v_cache, block_table, cu_seqlens_q, cu_s
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, T, int(max_seqlen_q), int(max_seqlen_k), NB, BS,
         HQ, HKV, D, float(scale), _dtype(q), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_set_debug_checks(on: bool) -> bool:
+    """Switch the debug checks of every launching entry point on or off for the process
+    (each call then synchronises to check its metadata); returns the previous setting."""
+    return bool(lib().pa_set_debug_checks(1 if on else 0))
 
 
 def pa_check_store_inputs(slot_mapping, num_blocks, block_size, stream=None):

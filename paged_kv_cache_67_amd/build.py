@@ -20,8 +20,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
-# the same library with PA_DEBUG_CHECKS: every entry point checks the device-side metadata first
-DEBUG_LIB = os.path.join(PKG, "libpa_debug.so")
 
 SOURCES = ["pa_status.cpp", "pa_blocks.cpp", "pa_check.cpp", "pa_store.hip", "pa_decode.hip",
            "pa_prefill.hip", "pa_mixed.hip"]
@@ -76,16 +74,6 @@ def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BU
     return out
 
 
-def build_debug(verbose: bool = False) -> str:
-    """libpa_debug.so: libpa built with PA_DEBUG_CHECKS (entry points synchronise to check
-    slot values, block ids and lengths before launching)."""
-    return build(verbose=verbose, defines=["PA_DEBUG_CHECKS"], out=DEBUG_LIB,
-                 build_dir=os.path.join(PKG, "_build_debug"))
-
-
 if __name__ == "__main__":
-    if "--debug-checks" in sys.argv[1:]:
-        build_debug(verbose=True)
-    else:
-        build(verbose=True)
+    build(verbose=True)
     sys.exit(0)

@@ -1,12 +1,16 @@
 // Debug checks of the device-side contract (slot values, block ids, lengths): the
 // metadata is copied to the host after the stream has drained and checked there.  The
 // kernels never need these (they stay in bounds whatever the metadata holds); they name
-// the first broken rule of a batch, for debugging and tests.  Building with
-// -DPA_DEBUG_CHECKS makes pa_store_kv, pa_decode, pa_decode_partitions, pa_prefill_paged
-// and pa_attention_mixed run them before every launch (which synchronises the stream and
-// so cannot be captured in a graph).
+// the first broken rule of a batch, for debugging and tests.  With the checks switched on
+// (PA_DEBUG_CHECKS set to anything but "0" in the environment when the library first looks,
+// or pa_set_debug_checks(1)), pa_store_kv, pa_decode, pa_decode_partitions,
+// pa_prefill_paged and pa_attention_mixed run them before every launch, which synchronises
+// the stream and so cannot be captured in a graph.
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
+#include <atomic>
 #include <unordered_set>
 #include <vector>
 
@@ -15,6 +19,21 @@
 #include "pa_internal.h"
 
 namespace pa {
+
+// -1: not looked at yet; 0 / 1: off / on.
+static std::atomic<int> g_debug{-1};
+
+bool debug_checks() {
+  int v = g_debug.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = getenv("PA_DEBUG_CHECKS");
+    const int env = e && *e && strcmp(e, "0") != 0 ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, env);
+    v = g_debug.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
 
 // Copies n int32 values from device memory after the stream has drained.
 static int fetch(std::vector<int32_t>& dst, const int32_t* src, int64_t n, hipStream_t s,
@@ -47,6 +66,12 @@ static int check_rows(const std::vector<int32_t>& bt, int32_t maxb, int32_t b, i
 using namespace pa;
 
 extern "C" {
+
+int pa_set_debug_checks(int on) {
+  const int prev = debug_checks() ? 1 : 0;
+  g_debug.store(on ? 1 : 0, std::memory_order_relaxed);
+  return prev;
+}
 
 int pa_check_store_inputs(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                           int32_t block_size, void* stream) {

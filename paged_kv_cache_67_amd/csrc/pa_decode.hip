@@ -320,11 +320,10 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
   if (!aligned16(out)) return fail(PA_ERR_ALIGN, "pa_decode: pointers must be 16-byte aligned");
   if ((st = validate_partition("pa_decode", partition_size))) return st;
   max_context_len = resolve_max_ctx(max_context_len, max_blocks_per_seq, block_size);
-#ifdef PA_DEBUG_CHECKS
-  if ((st = pa_check_decode_inputs(block_table, max_blocks_per_seq, context_lens, num_seqs,
+  if (debug_checks() &&
+      (st = pa_check_decode_inputs(block_table, max_blocks_per_seq, context_lens, num_seqs,
                                    max_context_len, num_blocks, block_size, stream)))
     return st;
-#endif
   const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
                                     max_context_len, partition_size, workspace != nullptr);
   const hipStream_t s = (hipStream_t)stream;
@@ -353,11 +352,10 @@ extern "C" int pa_decode_partitions(void* out, const void* q, const void* k_cach
   max_context_len = resolve_max_ctx(max_context_len, max_blocks_per_seq, block_size);
   if (partition_size == -1 || !workspace)
     return fail(PA_ERR_WORKSPACE, "pa_decode_partitions: a split needs a workspace");
-#ifdef PA_DEBUG_CHECKS
-  if ((st = pa_check_decode_inputs(block_table, max_blocks_per_seq, context_lens, num_seqs,
+  if (debug_checks() &&
+      (st = pa_check_decode_inputs(block_table, max_blocks_per_seq, context_lens, num_seqs,
                                    max_context_len, num_blocks, block_size, stream)))
     return st;
-#endif
   const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
                                     max_context_len, partition_size, true);
   if (pl.mode == DecodePlan::kSingle)

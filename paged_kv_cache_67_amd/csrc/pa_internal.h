@@ -16,6 +16,9 @@ int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)))
 void clear_error();
 // Check the launch that was just enqueued; returns PA_OK or PA_ERR_HIP.
 int check_launch(const char* what);
+// The debug checks of the device-side metadata are on (PA_DEBUG_CHECKS in the environment,
+// or pa_set_debug_checks).
+bool debug_checks();
 
 inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

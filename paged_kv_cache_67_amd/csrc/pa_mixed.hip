@@ -181,12 +181,11 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   if (!workspace || workspace_bytes < pl.ws_bytes)
     return fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
                 pl.ws_bytes);
-#ifdef PA_DEBUG_CHECKS
-  if (int cs = pa_check_prefill_inputs(block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
+  if (debug_checks())
+    if (int cs = pa_check_prefill_inputs(block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
                                        num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_blocks,
                                        block_size, stream))
-    return cs;
-#endif
+      return cs;
 
   const bool wide = block_size >= kPrefillKeys;
   mixed_fn kern = dtype == PA_F16 ? pick_mixed<PA_F16>(head_dim, wide, G)

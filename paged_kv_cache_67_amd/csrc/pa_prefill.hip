@@ -111,12 +111,11 @@ extern "C" int pa_prefill_paged(void* out, const void* q, const void* k_cache, c
     return fail(PA_ERR_NULL, "pa_prefill_paged: null pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PA_ERR_ALIGN, "pa_prefill_paged: pointers must be 16-byte aligned");
-#ifdef PA_DEBUG_CHECKS
-  if (int cs = pa_check_prefill_inputs(block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
+  if (debug_checks())
+    if (int cs = pa_check_prefill_inputs(block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
                                        num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_blocks,
                                        block_size, stream))
-    return cs;
-#endif
+      return cs;
   const int G = num_q_heads / num_kv_heads;
   const bool wide = block_size >= kPrefillKeys;
   prefill_fn fn = dtype == PA_F16 ? pick_prefill<PA_F16>(head_dim, wide, G)

@@ -134,10 +134,9 @@ extern "C" int pa_store_kv(const void* key, const void* value, int64_t key_token
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
       (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
     return fail(PA_ERR_ALIGN, "pa_store_kv: pointers and token strides must be 16-byte aligned");
-#ifdef PA_DEBUG_CHECKS
-  if (int cs = pa_check_store_inputs(slot_mapping, num_tokens, num_blocks, block_size, stream))
-    return cs;
-#endif
+  if (debug_checks())
+    if (int cs = pa_check_store_inputs(slot_mapping, num_tokens, num_blocks, block_size, stream))
+      return cs;
   const int row_chunks = int(row_bytes / 16);
   const int64_t items = (int64_t)num_tokens * row_chunks;
   const int64_t blocks = (items + 255) / 256;

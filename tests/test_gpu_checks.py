@@ -1,19 +1,16 @@
-"""Debug checks of the device-side contract (pa_check_*) and the PA_DEBUG_CHECKS build.
+"""Debug checks of the device-side contract (pa_check_*) and the entry points with the
+checks switched on.
 
 The checkers copy the metadata to the host and check it there; no kernel is ever
-launched on metadata that breaks the contract (with the debug library the entry
-point returns before its launch).
+launched on metadata that breaks the contract (with the checks on, the entry point
+returns before its launch).
 """
-
-import os
 
 import numpy as np
 import pytest
 import torch
 
 import paged_kv_cache_67_amd as pk
-from paged_kv_cache_67_amd import _binding as B
-from paged_kv_cache_67_amd import build as pkbuild
 from paged_kv_cache_67_amd import harness
 from tests.gpu_util import announce
 from workloads import make_workload
@@ -94,21 +91,18 @@ def test_check_prefill_inputs():
 
 
 @pytest.fixture()
-def debug_lib():
-    if not os.path.exists(pkbuild.DEBUG_LIB):
-        pytest.skip("libpa_debug.so is not built (python -m paged_kv_cache_67_amd.build --debug-checks)")
-    saved = (B._LIB_PATH, B._lib)
-    B._LIB_PATH, B._lib = pkbuild.DEBUG_LIB, None
+def checks_on():
+    prev = pk.pa_set_debug_checks(True)
     try:
-        yield B.lib()
+        yield
     finally:
-        B._LIB_PATH, B._lib = saved
+        pk.pa_set_debug_checks(prev)
 
 
-def test_debug_build_checks_before_launch(debug_lib):
-    """The PA_DEBUG_CHECKS library refuses broken metadata before any launch and computes
-    the same bits as the release library on good metadata."""
-    announce("libpa_debug: decode and prefill")
+def test_entry_points_check_before_launch(checks_on):
+    """With the checks on, the entry points refuse broken metadata before any launch and
+    compute the same bits as with them off on good metadata."""
+    announce("debug checks on: decode, store and prefill")
     w = make_workload(name="dbg", kind="decode", dtype="bf16", num_q_heads=4, num_kv_heads=2,
                       head_dim=64, block_size=16, seq_lens_k=[40, 1, 17], seed=11)
     dw = harness.DeviceWorkload(w, "cuda")
@@ -130,14 +124,13 @@ def test_debug_build_checks_before_launch(debug_lib):
         pk.pa_store_kv(dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, bad_slots)
     assert _status(e) == CONTRACT
 
-    saved = (B._LIB_PATH, B._lib)
-    B._LIB_PATH, B._lib = pkbuild.LIB, None
+    assert pk.pa_set_debug_checks(False)
     try:
         dw.out.zero_()
         dw.attention()
         torch.cuda.synchronize()
     finally:
-        B._LIB_PATH, B._lib = saved
+        pk.pa_set_debug_checks(True)
     assert torch.equal(got, dw.out)
 
     wp = make_workload(name="dbgp", kind="prefill", dtype="bf16", num_q_heads=4, num_kv_heads=2,
