@@ -12,6 +12,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte register chunk
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kPrefillRows = 128;     // query rows (position x head) per workgroup
 constexpr int kPrefillKeys = 128;     // keys per tile
@@ -496,10 +497,12 @@ __device__ __forceinline__ void prefill_body(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         r[i] = (o[qg][db][i] * a0 + mO[((rg * 2 + qg) * 4 * DB + 4 * db + i) * 64 + lane] * a1) * inv;
-      uint2 pk;
-      pk.x = uint32_t(M::bits(r[0])) | (uint32_t(M::bits(r[1])) << 16);
-      pk.y = uint32_t(M::bits(r[2])) | (uint32_t(M::bits(r[3])) << 16);
-      *reinterpret_cast<uint2*>(dst + 16 * db + 4 * grp) = pk;
+      const u32x2_t pk = {uint32_t(M::bits(r[0])) | (uint32_t(M::bits(r[1])) << 16),
+                          uint32_t(M::bits(r[2])) | (uint32_t(M::bits(r[3])) << 16)};
+      // Non-temporal: the output is not read again by this launch, and streaming it past
+      // the caches shortens the launch's end (31.4 -> 31.0 us with K/V cache-resident,
+      // 35.4 -> 33.8 us with K/V from HBM, on 8 x (1024 + 256) tokens).
+      __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_t*>(dst + 16 * db + 4 * grp));
     }
   }
 }
