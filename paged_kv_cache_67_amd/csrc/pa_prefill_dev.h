@@ -482,6 +482,15 @@ __device__ __forceinline__ void prefill_body(
   __syncthreads();
   if (kh == 1) return;
   const bool poisoned = s_bad != 0;
+  // The merged rows go to LDS in row-major order (16-byte chunks XOR-swizzled by row, so
+  // that neither side conflicts) and leave in 16-byte chunks per lane: each non-temporal
+  // store then writes whole 64-byte pieces of a row.  Wave rg stages its 32 rows in the
+  // last tile buffer, which the merge area does not reach.
+  constexpr int CR = D / 8;  // 16-byte chunks per output row
+  uint16_t* stage = sKV[3] + rg * 32 * D;
+  static_assert(4 * 32 * D <= BN * D, "staging area");
+  static_assert((4 * 2 * (4 * DB + 2) * 64) * sizeof(float) <= 3 * BN * D * sizeof(uint16_t),
+                "merge area below the staging area");
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
     const int rq = (rg * 2 + qg) * 64 + lane;
@@ -489,8 +498,7 @@ __device__ __forceinline__ void prefill_body(
     const float mm = fmaxf(m[qg], m1);
     const float a0 = fast_exp2(m[qg] - mm), a1 = fast_exp2(m1 - mm);
     const float inv = poisoned ? NAN : 1.0f / (lsum[qg][0] * a0 + mL[rq] * a1);
-    if (!rvalid[qg]) continue;
-    uint16_t* dst = out + (qtok[qg] * HQ + hq[qg]) * D;
+    const int rl = 16 * qg + qc;  // row within the wave's 32
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float r[4];
@@ -499,11 +507,21 @@ __device__ __forceinline__ void prefill_body(
         r[i] = (o[qg][db][i] * a0 + mO[((rg * 2 + qg) * 4 * DB + 4 * db + i) * 64 + lane] * a1) * inv;
       const u32x2_t pk = {uint32_t(M::bits(r[0])) | (uint32_t(M::bits(r[1])) << 16),
                           uint32_t(M::bits(r[2])) | (uint32_t(M::bits(r[3])) << 16)};
-      // Non-temporal: the output is not read again by this launch, and streaming it past
-      // the caches shortens the launch's end (31.4 -> 31.0 us with K/V cache-resident,
-      // 35.4 -> 33.8 us with K/V from HBM, on 8 x (1024 + 256) tokens).
-      __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_t*>(dst + 16 * db + 4 * grp));
+      const int c = 2 * db + (grp >> 1);  // 16-byte chunk of d = 16 db + 4 grp
+      *reinterpret_cast<u32x2_t*>(stage + rl * D + ((c ^ (rl % CR)) * 8) + 4 * (grp & 1)) = pk;
     }
+  }
+  // Each wave reads back only what it wrote (LDS keeps a wave's accesses in order).
+  constexpr int RPI = 64 / CR;  // rows per pass
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; ++it) {
+    const int rl = it * RPI + lane / CR, c = lane % CR;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + rl * D + ((c ^ (rl % CR)) * 8));
+    const int row = 32 * rg + rl;
+    const int rpos = row / G;
+    const int64_t tok = (int64_t)q0 + pos0 + rpos;
+    if (row < BM * G && rpos < npos && tok >= 0 && tok < total_q)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (tok * HQ + g * G + row % G) * D + 8 * c));
   }
 }
 
