@@ -18,10 +18,12 @@
  *   slot_mapping, context_lens, seq_lens_k and cu_seqlens_* are DEVICE
  *   pointers owned by the caller.  The library allocates no device memory,
  *   keeps no pointer after a call returns and has no mutable global state
- *   except a thread-local error message.
+ *   except a thread-local error message and the process-wide switch of the
+ *   debug checks (pa_set_debug_checks, off by default).
  * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *   stream): it validates its host-side arguments, enqueues its kernels and
- *   returns.  It performs no host<->device copies and no synchronisation.
+ *   returns.  It performs no host<->device copies and no synchronisation
+ *   (unless the debug checks are switched on; see pa_check_*).
  *   Inputs must stay alive and unchanged until the stream reaches the work.
  * - KV pool layout ([KVblog] 3.1: kv_cache is (2, layers, num_blocks,
  *   block_size, kv_heads, head_dim); one layer's K or V pool):
