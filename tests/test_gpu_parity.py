@@ -456,3 +456,41 @@ def test_mixed_serving_step_workload():
     announce(f"mixed serving step {w.name}")
     dw = _mixed_run(w)
     assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(True), "bf16", w.name)
+
+
+# ---------------------------------------------------------------------------
+# Random shapes through prefill and the mixed launch (seeded; each small enough for the oracle)
+
+def _random_case(seed):
+    r = np.random.default_rng(seed)
+    G = int(r.choice([1, 2, 3, 4, 5, 7, 8, 16]))
+    HKV = int(r.choice([1, 2, 4])) if G < 16 else 1
+    D = int(r.choice([64, 128]))
+    bs = int(r.choice([8, 16, 32, 64, 128, 256]))
+    B = int(r.integers(1, 5))
+    lk = r.integers(1, 700, size=B)
+    lq = np.array([int(r.integers(1, k + 1)) if r.random() < 0.7 else 1 for k in lk])
+    dtype = "f16" if r.random() < 0.3 else "bf16"
+    return dict(G=G, HKV=HKV, D=D, bs=bs, lk=lk.tolist(), lq=lq.tolist(), dtype=dtype)
+
+
+@pytest.mark.parametrize("seed", list(range(40)))
+def test_prefill_and_mixed_random_shapes(seed):
+    c = _random_case(1000 + seed)
+    w = make_workload(name="rand", kind="prefill", dtype=c["dtype"], num_q_heads=c["G"] * c["HKV"],
+                      num_kv_heads=c["HKV"], head_dim=c["D"], block_size=c["bs"],
+                      seq_lens_k=c["lk"], new_lens=c["lq"], seed=seed)
+    announce(f"random prefill/mixed case {seed}: {c}")
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    dw.slot_mapping()
+    dw.store()
+    want = OracleRun(w).prefill(True)
+    pk.pa_prefill_paged(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_table, dw.cu_q, dw.cu_k,
+                        w.max_seqlen_q, w.max_seqlen_k, w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert_close(out_f64(dw.out, c["dtype"]), want, c["dtype"], f"prefill {c}")
+    dw.out.zero_()
+    dw.attention_mixed()
+    torch.cuda.synchronize()
+    assert_close(out_f64(dw.out, c["dtype"]), want, c["dtype"], f"mixed {c}")
