@@ -422,16 +422,10 @@ def time_mixed(args):
             "timing": "HIP graph of the call(s), replayed between two events"}
 
 
-def cpu_baseline(w, dw, seconds):
-    """Time the CPU oracle on a bounded sample of the same batch; check the GPU on it too."""
+def _oracle_sample(w, kp, vp, gpu, seconds):
+    """The oracle's slot mapping, store and fp64 decode, sequence by sequence in a fixed
+    random order, until `seconds` have passed; returns what it did and its errors."""
     import oracle
-    from paged_kv_cache_67_amd import harness
-
-    log("cpu baseline: building oracle pools (not timed)")
-    kp, vp = w.empty_pool(), w.empty_pool()
-    oracle.store_kv(kp, vp, w.k_hist, w.v_hist,
-                    oracle.slot_mapping(w.block_table, w.cu_seqlens_hist, w.hist_lens, w.block_size))
-    gpu = oracle.to_f64(harness.from_device(dw.out), w.dtype)
     order = np.random.default_rng(0).permutation(w.num_seqs)
     done, errs, nbytes = [], [], 0
     wall0, cpu0 = time.perf_counter(), time.process_time()
@@ -447,13 +441,36 @@ def cpu_baseline(w, dw, seconds):
         if time.perf_counter() - wall0 >= seconds:
             break
     wall = time.perf_counter() - wall0
-    cpu = time.process_time() - cpu0
-    err = np.stack(errs)
+    return done, np.stack(errs), nbytes, wall, time.process_time() - cpu0
+
+
+def cpu_baseline(w, dw, seconds):
+    """Time the CPU oracle on a bounded sample of the same batch (all host threads, and
+    again on one thread for a shorter sample); check the GPU rows on it too."""
+    import oracle
+    from paged_kv_cache_67_amd import harness
+
+    log("cpu baseline: building oracle pools (not timed)")
+    kp, vp = w.empty_pool(), w.empty_pool()
+    oracle.store_kv(kp, vp, w.k_hist, w.v_hist,
+                    oracle.slot_mapping(w.block_table, w.cu_seqlens_hist, w.hist_lens, w.block_size))
+    gpu = oracle.to_f64(harness.from_device(dw.out), w.dtype)
+    done, err, nbytes, wall, cpu = _oracle_sample(w, kp, vp, gpu, seconds)
     log(f"cpu baseline: {len(done)} sequences in {wall:.1f} s; parity max {err.max():.2e} mean {err.mean():.2e}")
-    return ({"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-             "kind": "oracle",
-             "sample": f"{len(done)} of {w.num_seqs} sequences (random order, seed 0): slot mapping, "
-                       f"store and fp64 decode, {wall:.1f} s wall"},
+    base = {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {w.num_seqs} sequences (random order, seed 0): slot mapping, "
+                      f"store and fp64 decode, {wall:.1f} s wall"}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, _, n1, wall1, _ = _oracle_sample(w, kp, vp, gpu, min(seconds, 5.0))
+        base["one_thread"] = {"value": round(n1 / wall1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"first {len(d1)} sequences of the same order, {wall1:.1f} s wall"}
+        log(f"cpu baseline, one thread: {len(d1)} sequences in {wall1:.1f} s")
+    except ImportError:
+        pass
+    return (base,
             {"sample_seqs": len(done), "max_err": float(err.max()), "mean_err": float(err.mean()),
              "ok": bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and np.all(np.isfinite(gpu)))})
 
