@@ -37,7 +37,9 @@ struct Mfma<PA_BF16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __bf16 cvt(float x) { return (__bf16)x; }
-  __device__ static uint16_t bits(float x) { return f32_to_bf16(x); }
+  // The hardware conversion (v_cvt_pk_bf16_f32) rounds to nearest even, as the
+  // bit-level rounding of the other kernels does, in one instruction per pair.
+  __device__ static uint16_t bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 };
 template <>
 struct Mfma<PA_F16> {
