@@ -91,19 +91,14 @@ def test_decode_matches_oracle(idx):
     assert_close(got, want, w.dtype, f"cfg{idx}")
 
 
-def test_decode_qwen3_full_size_sampled():
-    """The benchmarked configuration (B=256, auto split-K) on a sample of sequences."""
+def test_decode_qwen3_full_size():
+    """The benchmarked configuration (B=256, auto split-K): every row against the oracle."""
     w = config(2)
-    announce("decode cfg2 full size, balanced split")
+    announce("decode cfg2 full size, balanced split, all 256 rows")
     dw = run_hip(w)
     got = out_f64(dw.out, w.dtype)
-    rng = np.random.default_rng(2)
-    lens = w.seq_lens_k
-    seqs = np.unique(np.concatenate([[np.argmin(lens), np.argmax(lens)],
-                                     rng.choice(w.num_seqs, 22, replace=False)]))
-    want = oracle_run(2).decode(seqs)
-    assert_close(got[seqs], want, w.dtype, "cfg2 sample")
-    assert np.all(np.isfinite(got))
+    want = oracle_run(2).decode()
+    assert_close(got, want, w.dtype, "cfg2")
 
 
 @pytest.mark.parametrize("idx,parts", [(1, [16, 64, 256, 1024, -1]), (3, [256, 1024, 8192, -1])])
