@@ -238,6 +238,39 @@ int pa_decode_merge(void* out, const void* workspace, const int32_t* context_len
                     int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                     pa_dtype dtype, void* stream);
 
+/* Bytes of the scratch array inside the library that pa_decode_noalloc uses (per device). */
+#define PA_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.
+ *
+ * Same arguments, meaning and results as pa_decode without the workspace: the
+ * split-K states go to a file-scope device array of PA_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library instead of a caller buffer.  Each device the library
+ * runs on holds its own copy of the array until the process ends; its address is
+ * looked up on the first call on that device (with that device current) and
+ * kept.  Nothing is allocated and nothing needs clearing: every state a call
+ * reads back was written earlier in the same call.
+ *
+ * Limit: a split whose workspace (pa_decode_workspace_size) exceeds
+ * PA_NOALLOC_SCRATCH_BYTES is refused with PA_ERR_WORKSPACE before any work is
+ * enqueued; a single-pass call (partition_size -1, or a context too short to
+ * split) uses no scratch.  For the Qwen3-0.6B shape (16 Q / 8 KV heads, head_dim
+ * 128) the balanced split needs about 4.3 MB at any batch up to 8192.
+ *
+ * Every call on one device shares that device's array: calls that overlap on a
+ * device (two streams, or two host threads) race and must be ordered by the
+ * caller.  Returns PA_ERR_HIP if the array's address cannot be looked up.
+ */
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, float scale, pa_dtype dtype,
+                      int32_t partition_size, void* stream);
+
 /*
  * pa_prefill_paged -- varlen (chunked) prefill attention over a cached prefix.
  *

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     pa_copy_blocks,
     pa_decode,
     pa_decode_merge,
+    pa_decode_noalloc,
     pa_decode_partitions,
     pa_decode_workspace_size,
     pa_last_error,

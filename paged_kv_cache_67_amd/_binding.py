@@ -38,6 +38,8 @@ SIGNATURES = {
     "pa_decode_partitions": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
     "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _f32, C.c_int, _i32, _vp]),
     "pa_prefill_paged": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                    _i32, _i32, _i32, _i32, _i32, _f32, _i32, C.c_int, _vp]),
     "pa_mixed_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -179,6 +181,21 @@ def pa_decode(out, q, k_cache, v_cache, block_table, context_lens, scale, max_co
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(context_lens), B, int(max_context_len), NB, BS, HQ, HKV, D, float(scale),
         _dtype(q), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_table, context_lens, scale, max_context_len=0,
+                      partition_size=0, stream=None):
+    B, HQ, D = q.shape
+    NB, BS, HKV, Dk = k_cache.shape
+    assert out.shape == q.shape and Dk == D and v_cache.shape == k_cache.shape
+    assert q.is_contiguous() and out.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
+    assert out.dtype == q.dtype == k_cache.dtype == v_cache.dtype
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.shape[0] == B
+    _i32_vec(context_lens, B, "context_lens")
+    _check("pa_decode_noalloc", lib().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(context_lens), B, int(max_context_len), NB, BS, HQ, HKV, D, float(scale), _dtype(q),
+        int(partition_size), _stream(stream)))
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, scale, max_context_len,

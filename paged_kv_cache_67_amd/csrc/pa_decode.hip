@@ -26,6 +26,8 @@
 //    workspace layout documented in pa.h.
 #include <limits.h>
 
+#include <mutex>
+
 #include "pa_decode_plan.h"
 
 namespace pa {
@@ -394,4 +396,80 @@ extern "C" int pa_decode_merge(void* out, const void* workspace, const int32_t* 
   }
   return launch_merge(out, pl, carve(const_cast<void*>(workspace), pl, num_seqs, num_q_heads, head_dim),
                       context_lens, num_seqs, num_q_heads, head_dim, dtype, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: pa_decode with its split-K workspace in a fixed array inside the
+// library, for callers that cannot allocate.  The array lives in device global memory (one
+// copy per device the library runs on, held until the process ends); host code never uses
+// its name as an address: each device's address is looked up once, with that device
+// current, and kept.
+
+namespace pa {
+
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];  // per device, filled on the first call there
+
+// The device address of `scratch` on the current device (looked up once per device).
+static int scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array: %s", fn,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" int pa_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t max_context_len, int32_t num_blocks,
+                                 int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float scale, pa_dtype dtype,
+                                 int32_t partition_size, void* stream) {
+  const char* fn = "pa_decode_noalloc";
+  clear_error();
+  int st = validate_decode(fn, q, k_cache, v_cache, block_table, max_blocks_per_seq, context_lens,
+                           num_seqs, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                           dtype, nullptr);
+  if (st || num_seqs == 0) return st;
+  if (!out) return fail(PA_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned16(out)) return fail(PA_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if ((st = validate_partition(fn, partition_size))) return st;
+  max_context_len = resolve_max_ctx(max_context_len, max_blocks_per_seq, block_size);
+  // The plan of pa_decode with a workspace; refused before any HIP call when its workspace
+  // would not fit in the array.
+  const DecodePlan pl = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, dtype,
+                                    max_context_len, partition_size, true);
+  if (pl.mode != DecodePlan::kSingle && pl.ws_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE, "%s: the split needs %zu bytes of scratch, the library's "
+                "array holds %d (use pa_decode with a workspace, or partition_size -1)",
+                fn, pl.ws_bytes, PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (pl.mode != DecodePlan::kSingle && (st = scratch_on_current_device(fn, &ws))) return st;
+  if (debug_checks() &&
+      (st = pa_check_decode_inputs(block_table, max_blocks_per_seq, context_lens, num_seqs,
+                                   max_context_len, num_blocks, block_size, stream)))
+    return st;
+  const hipStream_t s = (hipStream_t)stream;
+  st = launch_decode(fn, pl, out, q, k_cache, v_cache, block_table, max_blocks_per_seq,
+                     context_lens, num_seqs, num_blocks, block_size, num_q_heads, num_kv_heads,
+                     head_dim, scale, dtype, ws, PA_NOALLOC_SCRATCH_BYTES, s);
+  if (st || pl.mode == DecodePlan::kSingle) return st;
+  return launch_merge(out, pl, carve(ws, pl, num_seqs, num_q_heads, head_dim), context_lens,
+                      num_seqs, num_q_heads, head_dim, dtype, s);
 }

@@ -28,6 +28,8 @@ constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 
 constexpr int kNumXCDs = 8;
 
+constexpr int kMaxDevices = 64;  // devices one process can drive (per-device state tables)
+
 // ---------------------------------------------------------------------------
 // Device side.
 

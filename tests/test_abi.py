@@ -93,6 +93,10 @@ def test_null_and_shape_errors(L):
     assert mixed(2, 9, 4, 8, 4, 2, 128, 1) == 2      # total_q > num_seqs * max_seqlen_q
     assert mixed(2, 8, 4, 8, 4, 2, 128, 1) == 1
     assert mixed(0, 0, 4, 8, 4, 2, 128, 1) == 0
+    # pa_decode_noalloc: the same host validation as pa_decode
+    assert L.pa_decode_noalloc(None, None, None, None, None, 4, None, 2, 0, 8, 16, 3, 2, 64, 0.1, 0, 0, None) == 2
+    assert L.pa_decode_noalloc(None, None, None, None, None, 4, None, 2, 0, 8, 16, 4, 2, 64, 0.1, 1, 0, None) == 1
+    assert L.pa_decode_noalloc(None, None, None, None, None, 4, None, 0, 0, 8, 16, 4, 2, 64, 0.1, 1, 0, None) == 0
 
 
 def _gpu_visible():
@@ -123,6 +127,12 @@ def test_alignment_and_workspace_errors(L):
     assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, 2, 8, 4, 64, 8, 16, 4, 2, 128, 0.1, 1, None, 0, None) == 5
     assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, 2, 8, 4, 64, 8, 16, 4, 2, 128, 0.1, 1, a, needm - 4, None) == 5
     assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, 2, 8, 4, 64, 8, 16, 4, 2, 128, 0.1, 1, mis, needm, None) == 4
+    # the allocation-free decode refuses a split larger than its array before any HIP call
+    big = L.pa_decode_workspace_size(512, 16, 8, 128, 4096, 16)
+    assert big > 16 << 20
+    assert L.pa_decode_noalloc(a, a, a, a, a, 16, a, 512, 4096, 8, 256, 16, 8, 128, 0.1, 1, 16, None) == 5
+    assert "scratch" in pk.pa_last_error()
+    assert L.pa_decode_noalloc(a, a, a, mis, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, None) == 4
 
 
 def test_workspace_size_closed_form(L):
