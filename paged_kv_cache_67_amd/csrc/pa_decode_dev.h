@@ -87,9 +87,20 @@ struct Elem<PA_F32> {
 #ifndef PA_DECODE_LOADS
 #define PA_DECODE_LOADS 4
 #endif
-#ifndef PA_DECODE_WAVES_PER_CU
-#define PA_DECODE_WAVES_PER_CU 8
+// Waves of the balanced split over the whole chip (slices x head waves, 8 per workgroup):
+// a batch that may read more than the 256 MiB Infinity Cache is bound by HBM and runs
+// fastest on 192 of the 256 compute units (measured on the 256-row Qwen3-0.6B decode:
+// 346.5 us with 1536 waves, 355.8 us with 2048, 364.1 us with 1280; the skewed 32768 + 7 x 512
+// batch: 33.2 us against 34.1 us), while a batch that fits the cache is bound by latency
+// and wants every compute unit (batch 64 of Qwen2.5-0.5B: 24.5 us with 2048 waves, 25.7 us
+// with 1536).
+#ifndef PA_DECODE_WAVE_SLOTS
+#define PA_DECODE_WAVE_SLOTS 2048
 #endif
+#ifndef PA_DECODE_WAVE_SLOTS_HBM
+#define PA_DECODE_WAVE_SLOTS_HBM 1536
+#endif
+constexpr int64_t kInfinityCacheBytes = 256ll << 20;
 
 // Load slots per chunk: wide GQA tiles hold more q / state registers, so they
 // take smaller chunks to stay clear of spills and keep two waves per SIMD (a
@@ -346,62 +357,72 @@ __device__ __forceinline__ Cursor cursor_next(Cursor c, int B, const int* s_cuc,
   return c;
 }
 
-// One wave's slice of the balanced split: slice w of head wave hw (a KV head
-// and a G-wide tile of its query heads).  Every wave of the workgroup runs the
-// length scan and its barrier first.  VARLEN: the batch is varlen (cu_q, cu_k);
-// a sequence with exactly one query (a decode row, q row cu_q[b]) attends its
-// cu_k length of keys, any other sequence counts as empty here.  Otherwise
-// sequence b attends context_lens[b] keys with q / out row b.
+// The length scan of the balanced split, run by wave 0 (threads 0-63) of a workgroup:
+// s_mem[0 .. B] = s_cuc, the exclusive prefix sums of the chunk counts ceil(L_b / CH);
+// s_mem[B + 1 .. 2B] = s_len, the key counts L_b; VARLEN: s_mem[2B + 1 .. 3B] = s_row, the
+// q / out rows.  Each lane sums a contiguous segment of sequences and a wave-wide scan of
+// the segment sums gives each segment's offset.  VARLEN: the batch is varlen (cu_q, cu_k);
+// a sequence with exactly one query (a decode row, q row cu_q[b]) attends its cu_k length
+// of keys, any other sequence counts as empty here, and visit(nq, nk, L) sees each
+// sequence's query and key counts and its decode key count.  Otherwise sequence b attends
+// context_lens[b] keys with q / out row b.  Returns the total chunk count (every lane).
+template <int CH, bool VARLEN, typename Visit>
+__device__ __forceinline__ int balanced_scan(int* s_mem, const int32_t* __restrict__ context_lens,
+                                              const int32_t* __restrict__ cu_q,
+                                              const int32_t* __restrict__ cu_k, int total_q,
+                                              int B, Visit visit) {
+  int* s_cuc = s_mem;
+  int* s_len = s_mem + B + 1;
+  int* s_row = s_mem + 2 * B + 1;
+  const int lane = threadIdx.x;
+  const int seg = (B + 63) / 64;
+  const int lo = min(B, lane * seg), hi = min(B, lo + seg);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) {
+    int L;
+    if constexpr (VARLEN) {
+      const int q0 = cu_q[i], nq = cu_q[i + 1] - q0, nk = cu_k[i + 1] - cu_k[i];
+      L = nq == 1 && q0 >= 0 && q0 < total_q ? max(nk, 0) : 0;
+      s_row[i] = q0;
+      visit(nq, nk, L);
+    } else {
+      L = max(context_lens[i], 0);
+    }
+    s_len[i] = L;
+    sum += (L + CH - 1) / CH;
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  int run = incl - sum;
+  for (int i = lo; i < hi; ++i) {
+    s_cuc[i] = run;
+    run += (s_len[i] + CH - 1) / CH;
+  }
+  if (lane == 63) s_cuc[B] = incl;
+  return __shfl(incl, 63);
+}
+
+// One wave's slice of the balanced split, after the length scan (balanced_scan) and a
+// barrier: slice w of head wave hw (a KV head and a G-wide tile of its query heads), over
+// the tables at s_mem.  write_cuc: this workgroup also leaves s_cuc in the workspace for
+// the merge.
 template <int D, int ET, int G, bool VARLEN>
-__device__ __forceinline__ void decode_balanced_body(
-    int w, int hw, bool write_cuc, void* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_cuc,
-    const void* __restrict__ qptr, const void* __restrict__ kcache,
-    const void* __restrict__ vcache, const int32_t* __restrict__ block_table, int maxb,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int total_q, int B, int num_blocks, int bs_log2, int HQ,
-    int HKV, int group, float scale_log2, int Wt) {
+__device__ __forceinline__ void decode_balanced_run(
+    const int* s_mem, int w, int hw, bool write_cuc, void* __restrict__ out,
+    float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    int32_t* __restrict__ ws_cuc, const void* __restrict__ qptr, const void* __restrict__ kcache,
+    const void* __restrict__ vcache, const int32_t* __restrict__ block_table, int maxb, int B,
+    int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt) {
   using W = DecodeWave<D, ET, G>;
   constexpr int CH = W::CH;
   constexpr int U = W::U;
-  extern __shared__ int s_mem[];
-  int* s_cuc = s_mem;          // [B + 1] exclusive prefix sums of chunk counts
-  int* s_len = s_mem + B + 1;  // [B] key counts
-  int* s_row = VARLEN ? s_mem + 2 * B + 1 : nullptr;  // [B] q / out rows
-
-  // Wave 0 scans the chunk counts: each lane sums a contiguous segment, a
-  // wave-wide scan of the segment sums gives each segment's offset.
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int seg = (B + 63) / 64;
-    const int lo = min(B, lane * seg), hi = min(B, lo + seg);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) {
-      int L;
-      if constexpr (VARLEN) {
-        const int q0 = cu_q[i];
-        L = cu_q[i + 1] - q0 == 1 && q0 >= 0 && q0 < total_q ? max(cu_k[i + 1] - cu_k[i], 0) : 0;
-        s_row[i] = q0;
-      } else {
-        L = max(context_lens[i], 0);
-      }
-      s_len[i] = L;
-      sum += (L + CH - 1) / CH;
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    int run = incl - sum;
-    for (int i = lo; i < hi; ++i) {
-      s_cuc[i] = run;
-      run += (s_len[i] + CH - 1) / CH;
-    }
-    if (lane == 63) s_cuc[B] = incl;
-  }
-  __syncthreads();
+  const int* s_cuc = s_mem;
+  const int* s_len = s_mem + B + 1;
+  const int* s_row = VARLEN ? s_mem + 2 * B + 1 : nullptr;
   if (write_cuc)
     for (int i = threadIdx.x; i <= B; i += blockDim.x) ws_cuc[i] = s_cuc[i];
 
@@ -481,6 +502,27 @@ __device__ __forceinline__ void decode_balanced_body(
     st.compute(A, c0.j * CH, c0.L);
     finish(c0, c1);
   }
+}
+
+// The whole balanced-split slice for a standalone launch: every wave of the workgroup
+// takes part in the length scan's barrier, then runs its slice.
+template <int D, int ET, int G, bool VARLEN>
+__device__ __forceinline__ void decode_balanced_body(
+    int w, int hw, bool write_cuc, void* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_cuc,
+    const void* __restrict__ qptr, const void* __restrict__ kcache,
+    const void* __restrict__ vcache, const int32_t* __restrict__ block_table, int maxb,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int total_q, int B, int num_blocks, int bs_log2, int HQ,
+    int HKV, int group, float scale_log2, int Wt) {
+  extern __shared__ int s_mem[];
+  if (threadIdx.x < 64)
+    balanced_scan<DecodeWave<D, ET, G>::CH, VARLEN>(s_mem, context_lens, cu_q, cu_k, total_q, B,
+                                                     [](int, int, int) {});
+  __syncthreads();
+  decode_balanced_run<D, ET, G, VARLEN>(s_mem, w, hw, write_cuc, out, ws_acc, ws_m, ws_l, ws_cuc,
+                                        qptr, kcache, vcache, block_table, maxb, B, num_blocks,
+                                        bs_log2, HQ, HKV, group, scale_log2, Wt);
 }
 
 
@@ -583,7 +625,8 @@ __device__ __forceinline__ void merge_states(void* __restrict__ out, int64_t row
 // With w0 == w1 the decode pass already wrote the row; otherwise its pieces
 // are slice w0's tail state and slices w0+1 .. w1's head states.  VARLEN: only
 // the one-query sequences of a varlen batch are decode rows (row cu_q[b]); the
-// others belong to the prefill side and are left alone.
+// others belong to the prefill side and are left alone, and the slice count is the one
+// the first pass stored after its scan (Wt is then unused).
 template <int ET, bool VARLEN, int W>
 __global__ __launch_bounds__(64 * W) void merge_balanced_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_m,
@@ -603,11 +646,13 @@ __global__ __launch_bounds__(64 * W) void merge_balanced_kernel(
     return;
   }
   const int NC = ws_cuc[B];
-  const int Cw = (NC + Wt - 1) / Wt;
+  // A mixed launch picks its slice count on the device and leaves it after the scan.
+  const int nw = VARLEN ? ws_cuc[B + 1] : Wt;
+  const int Cw = (NC + nw - 1) / nw;
   const int w0 = cb / Cw, w1 = (ce - 1) / Cw;
   if (w0 == w1) return;
   // Piece 0 is the tail slot of slice w0, piece k >= 1 the head slot of slice w0 + k.
-  const int64_t base = (int64_t)h * Wt * 2 + (int64_t)w0 * 2;
+  const int64_t base = (int64_t)h * nw * 2 + (int64_t)w0 * 2;
   merge_states<ET, W>(out, row, ws_acc, ws_m, ws_l, w1 - w0 + 1, D, [&](int k) {
     return base + 2 * k + (k == 0 ? kTailSlot : kHeadSlot);
   });

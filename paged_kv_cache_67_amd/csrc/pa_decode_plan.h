@@ -40,13 +40,18 @@ inline DecodePlan plan_decode(int32_t B, int32_t HQ, int32_t HKV, int32_t D, pa_
     pl.mode = DecodePlan::kBalanced;
     const int head_waves = HKV * (group / pl.G);
     const int CH = chunk_tokens(D, elt_bytes(dtype), pl.G);
-    int64_t Wt = (int64_t)kNumCUs * PA_DECODE_WAVES_PER_CU / head_waves;
+    // Upper bound of the K and V bytes the batch reads (every sequence at max_ctx keys).
+    const double kv_bytes = (double)B * (max_ctx > 0 ? max_ctx : 1) * HKV * D * elt_bytes(dtype) * 2;
+    const int slots =
+        kv_bytes > (double)kInfinityCacheBytes ? PA_DECODE_WAVE_SLOTS_HBM : PA_DECODE_WAVE_SLOTS;
+    int64_t Wt = (int64_t)slots / head_waves;
     Wt = Wt < 1 ? 1 : Wt;
     const int64_t max_chunks = (int64_t)B * ceil_div(max_ctx > 0 ? max_ctx : 1, CH);
     if (Wt > max_chunks) Wt = max_chunks;
     pl.Wt = (int)Wt;
     const size_t states = (size_t)HQ * pl.Wt * 2;
-    pl.ws_bytes = states * (D + 2) * sizeof(float) + (size_t)(B + 1) * sizeof(int32_t);
+    // States, then the chunk scan s_cuc [B + 1] and the slice count the first pass used.
+    pl.ws_bytes = states * (D + 2) * sizeof(float) + (size_t)(B + 2) * sizeof(int32_t);
   } else {
     pl.P = partition_size > 0 ? partition_size : auto_partition(B, HKV, max_ctx);
     if (pl.P >= max_ctx) {
@@ -60,7 +65,8 @@ inline DecodePlan plan_decode(int32_t B, int32_t HQ, int32_t HKV, int32_t D, pa_
   return pl;
 }
 
-// Workspace carving: balanced = acc | m | l | cuc; fixed = acc | m | l.
+// Workspace carving: balanced = acc | m | l | cuc (B + 1 scan entries, then the slice
+// count of a mixed launch); fixed = acc | m | l.
 struct WsPtrs {
   float *acc, *m, *l;
   int32_t* cuc;

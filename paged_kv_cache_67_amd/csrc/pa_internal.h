@@ -22,7 +22,7 @@ bool debug_checks();
 
 inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-inline int elt_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+__host__ __device__ constexpr inline int elt_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 
 constexpr int kNumCUs = 256;  // MI355X: 8 XCDs x 32 CUs
 

@@ -9,49 +9,161 @@
 // 5), so one batch can hold prompt chunks and decode rows with no per-batch
 // prefill/decode switch.
 //
-// MI355X design.  One grid of 512-thread workgroups: the first ones run the
-// balanced split-K decode body over the sequences with Lq = 1 (each wave one
-// (slice, KV-head tile) of the flattened decode keys), the last n_pf (at most one
-// per compute unit) walk the list of query tiles of the sequences with Lq > 1
-// (MFMA prefill body).  Workgroups are handed out in launch order, so the
-// latency-bound prefill tiles take the compute units that the bandwidth-bound
-// decode slices free in the decode's tail, and no workgroup is launched for a
-// decode row's would-be prefill tile (measured on 256 decode rows + 8 x 256-token
-// chunks: 384 us, against 386 us as two launches, 395 us with half the compute
-// units on prefill tiles first and 414 us with all of them).  Decode rows cut by
-// slice boundaries leave partial states in the workspace; a second small launch
-// merges them.
+// MI355X design.  One grid of at most one 512-thread workgroup per compute unit (the
+// prefill tiles' LDS allows no more), all resident at once.  Every workgroup first scans
+// the batch's lengths (the decode chunk table of the balanced split, and the totals of
+// decode keys and prefill query-key pairs) and from those totals picks, with the same
+// arithmetic in every workgroup, how many workgroups take each side: the first ones run
+// the balanced split-K decode body over the sequences with Lq = 1 (each wave one (slice,
+// KV-head tile) of the flattened decode keys), the last n_pf walk the list of query tiles
+// of the sequences with Lq > 1 (MFMA prefill body).  The decode rows are bound by HBM and
+// reach its bandwidth on about 160-192 compute units; the prefill tiles are bound by the
+// matrix cores and LDS of their own compute unit and read little, so the two sides run
+// side by side and the step takes about the longer of the two instead of their sum.  The
+// split minimises the larger of the two modelled times (decode bytes over the bandwidth
+// of its workgroups, rounds of prefill tiles times the mean tile's flops over a
+// workgroup's rate).  Decode rows cut by slice boundaries leave partial states in the
+// workspace; a second small launch merges them.
+#include <algorithm>
+#include <mutex>
+#include <unordered_set>
+
 #include "pa_decode_plan.h"
 #include "pa_prefill_dev.h"
 
 namespace pa {
 
-constexpr int kMaxMixedSeqs = 4096;  // LDS holds 3 ints per sequence beside the prefill tiles
+// Rates of the split's cost model, measured on MI355X: decode K/V bytes per ns of one
+// decode workgroup (eight waves) and of the whole chip, and flops per ns of one prefill
+// workgroup.
+constexpr float kDecBytesPerNsWG = 40.0f;
+constexpr float kDecBytesPerNsChip = 6500.0f;
+constexpr float kPfFlopsPerNsWG = 2100.0f;
+
+constexpr int kMaxLdsBytes = 160 * 1024;  // LDS one workgroup may hold (gfx950)
+// Dynamic LDS of a mixed workgroup: the split (4 ints), then the decode tables
+// (3 * num_seqs + 1 ints; the prefill side reuses their first num_seqs + 1 for its tile scan).
+inline size_t mixed_dyn_lds(int B) { return (size_t)(3 * B + 5) * sizeof(int); }
+// The most sequences a mixed launch takes at head size D: the dynamic LDS beside the
+// prefill body's static LDS stays within one workgroup's LDS.
+constexpr int mixed_max_seqs(int D) {
+  const int by_lds = ((kMaxLdsBytes - prefill_lds_bytes(D)) / (int)sizeof(int) - 5) / 3;
+  return by_lds < kMaxBalancedSeqs ? by_lds : kMaxBalancedSeqs;
+}
+
+// Query heads per decode wave in a mixed launch: as in pa_decode, except that groups of 8
+// and 16 take tiles of 4 heads.  An 8-head tile wants more than the 256 VGPRs a wave of a
+// 512-thread workgroup may hold (pa_decode runs it in 256-thread workgroups); two 4-head
+// waves of one KV head read the same K/V rows at about the same time, so the second read
+// is served by the L2.
+__host__ __device__ constexpr int mixed_head_tile(int G) { return G >= 8 ? 4 : head_tile(G); }
 
 template <int D, int G, bool WIDE, int ET>
 __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ block_table, int maxb,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int total_q, int B,
-    int num_blocks, int bs_log2, int HQ, int HKV, float scale_log2, int n_pf,
+    int num_blocks, int bs_log2, int HQ, int HKV, float scale_log2,
     float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    int32_t* __restrict__ ws_cuc, int head_waves, int Wt) {
-  const int pf_id = (int)blockIdx.x - ((int)gridDim.x - n_pf);  // prefill workers come last
-  if (pf_id >= 0) {
-    // Prefill workgroups walk a list of the batch's query tiles, built here from cu_q: a
-    // sequence with Lq >= 2 has ceil(Lq / BM) tiles per KV head.  Items are numbered
-    // sequence, then KV head, then tile, and handed out so that consecutive items run on
-    // one XCD (tiles of one sequence and KV head read the same K/V rows through its L2).
-    constexpr int BM = kPrefillRows / G;
-    // [B + 1] exclusive prefix sums of tiles per sequence.
-    extern __shared__ int s_items[];
+    int32_t* __restrict__ ws_cuc, int head_waves, int Wt_max, int dec_wgs_max) {
+  constexpr int GT = mixed_head_tile(G);
+  constexpr int CH = DecodeWave<D, ET, GT>::CH;
+  constexpr int BM = kPrefillRows / G;
+  constexpr int WAVES = kPrefillThreads / 64;
+  extern __shared__ int s_dyn[];
+  int* s_split = s_dyn;    // [0]: prefill workgroups
+  int* s_mem = s_dyn + 4;  // decode tables, later the prefill tile scan
+  const int n_wg = gridDim.x;
+  const int i = blockIdx.x;
+
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int tiles = 0;
+    float pairs = 0.0f, dec_keys = 0.0f;
+    const int dec_chunks = balanced_scan<CH, true>(
+        s_mem, nullptr, cu_q, cu_k, total_q, B, [&](int nq, int nk, int L) {
+          dec_keys += (float)L;
+          if (nq >= 2) {  // causal query-key pairs of a chunk of nq queries over nk keys
+            const float fq = (float)nq;
+            tiles += (nq + BM - 1) / BM;
+            pairs += fq * (float)(nk - nq) + 0.5f * fq * (fq + 1.0f);
+          }
+        });
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      tiles += __shfl_xor(tiles, o);
+      pairs += __shfl_xor(pairs, o);
+      dec_keys += __shfl_xor(dec_keys, o);
+    }
+    const int items = tiles * HKV;
+    int n_pf;
+    if (items == 0) {
+      n_pf = 0;
+    } else if (dec_chunks == 0) {
+      n_pf = n_wg;
+    } else {
+      // Candidates: n_pf in [lo, hi], multiples of 8 on a full chip (each XCD then holds
+      // the same share of both sides); each lane prices some, the cheapest wins (ties to
+      // fewer prefill workgroups).
+      const int min_dec = (head_waves + WAVES - 1) / WAVES;
+      const int lo = max(1, n_wg - dec_wgs_max), hi = n_wg - min_dec;
+      const int step = n_wg >= 64 ? 8 : 1;
+      const float dec_bytes = dec_keys * (float)(HKV * D * 2 * elt_bytes((pa_dtype)ET));
+      const float tile_ns = pairs * (float)(HQ * D * 4) / (float)items / kPfFlopsPerNsWG;
+      float best_t = __builtin_huge_valf();
+      int best_n = lo;
+      for (int c = (lo + step - 1) / step * step + lane * step; c <= hi; c += 64 * step) {
+        const int nd = min(n_wg - c, dec_wgs_max);
+        const float t_dec = dec_bytes / fminf(kDecBytesPerNsChip, (float)nd * kDecBytesPerNsWG);
+        const float t_pf = (float)((items + c - 1) / c) * tile_ns;
+        const float t = fmaxf(t_dec, t_pf);
+        if (t < best_t) {
+          best_t = t;
+          best_n = c;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ot = __shfl_xor(best_t, o);
+        const int on = __shfl_xor(best_n, o);
+        if (ot < best_t || (ot == best_t && on < best_n)) {
+          best_t = ot;
+          best_n = on;
+        }
+      }
+      n_pf = best_n;
+#ifdef PA_MIXED_PF_WGS  // calibration builds: a fixed prefill share
+      n_pf = min(max(PA_MIXED_PF_WGS, lo), hi);
+#endif
+    }
+    if (lane == 0) s_split[0] = n_pf;
+  }
+  __syncthreads();
+  const int n_pf = lds_uniform(s_split);
+  const int n_dec = min(n_wg - n_pf, dec_wgs_max);
+  // Slices per head wave of the decode side (n_dec * WAVES >= head_waves whenever there
+  // are decode keys, so every head wave has a slice).
+  const int Wt = max(1, min(Wt_max, n_dec * WAVES / head_waves));
+  if (i == 0) {  // the chunk scan and slice count for the merge
+    for (int k = threadIdx.x; k <= B; k += blockDim.x) ws_cuc[k] = s_mem[k];
+    if (threadIdx.x == 0) ws_cuc[B + 1] = Wt;
+  }
+
+  if (i >= n_wg - n_pf) {
+    // Prefill workgroups walk a list of the batch's query tiles: a sequence with Lq >= 2
+    // has ceil(Lq / BM) tiles per KV head.  Items are numbered sequence, then KV head, then
+    // tile, and handed out so that consecutive items run on one XCD (tiles of one sequence
+    // and KV head read the same K/V rows through its L2).
+    const int pf_id = i - (n_wg - n_pf);
+    int* s_items = s_mem;  // [B + 1] exclusive prefix sums of tiles per sequence
+    __syncthreads();       // the decode tables are no longer read
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
       const int seg = (B + 63) / 64;
       const int lo = min(B, lane * seg), hi = min(B, lo + seg);
       int sum = 0;
-      for (int i = lo; i < hi; ++i) {
-        const int Lq = cu_q[i + 1] - cu_q[i];
+      for (int k = lo; k < hi; ++k) {
+        const int Lq = cu_q[k + 1] - cu_q[k];
         sum += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
       }
       int incl = sum;
@@ -61,9 +173,9 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
         if (lane >= o) incl += v;
       }
       int run = incl - sum;
-      for (int i = lo; i < hi; ++i) {
-        s_items[i] = run;
-        const int Lq = cu_q[i + 1] - cu_q[i];
+      for (int k = lo; k < hi; ++k) {
+        s_items[k] = run;
+        const int Lq = cu_q[k + 1] - cu_q[k];
         run += Lq >= 2 ? (Lq + BM - 1) / BM : 0;
       }
       if (lane == 63) s_items[B] = incl;
@@ -80,23 +192,27 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
       const int first = lds_uniform(s_items + lo);
       const int T = lds_uniform(s_items + lo + 1) - first;
       const int r = j - HKV * first;
-      prefill_body<D, G, WIDE, true, ET>(r % T, r / T, lo, out, q, kc, vc, block_table, maxb, cu_q,
-                                     cu_k, total_q, num_blocks, bs_log2, HQ, HKV, scale_log2, 1);
+      // The thread index passes through an empty asm so that the body's lane-dependent
+      // setup is redone per item instead of being hoisted out of the loop (it would then
+      // stay live across every item and spill).
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      prefill_body<D, G, WIDE, true, ET>(tid, r % T, r / T, lo, out, q, kc, vc, block_table, maxb,
+                                         cu_q, cu_k, total_q, num_blocks, bs_log2, HQ, HKV,
+                                         scale_log2, 1);
       __syncthreads();  // the next item reuses this item's LDS
     }
-  } else {
-    const int i = blockIdx.x;
-    const int item = i * (kPrefillThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    decode_balanced_body<D, ET, head_tile(G), true>(
-        item / head_waves, item % head_waves, i == 0, out, ws_acc, ws_m, ws_l, ws_cuc, q, kc, vc,
-        block_table, maxb, nullptr, cu_q, cu_k, total_q, B, num_blocks, bs_log2, HQ, HKV, G,
-        scale_log2, Wt);
+  } else if (i < n_dec) {
+    const int item = i * WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    decode_balanced_run<D, ET, GT, true>(s_mem, item / head_waves, item % head_waves, false, out,
+                                         ws_acc, ws_m, ws_l, ws_cuc, q, kc, vc, block_table, maxb,
+                                         B, num_blocks, bs_log2, HQ, HKV, G, scale_log2, Wt);
   }
 }
 
 typedef void (*mixed_fn)(uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
                          const int32_t*, int, const int32_t*, const int32_t*, int, int, int, int,
-                         int, int, float, int, float*, float*, float*, int32_t*, int, int);
+                         int, int, float, float*, float*, float*, int32_t*, int, int, int);
 
 template <int D, bool WIDE, int ET>
 static mixed_fn pick_mixed_g(int G) {
@@ -120,6 +236,23 @@ static mixed_fn pick_mixed(int D, bool wide, int G) {
   return wide ? pick_mixed_g<128, true, ET>(G) : pick_mixed_g<128, false, ET>(G);
 }
 
+// The launch's LDS (static + dynamic) stays within a workgroup's only if the kernel's
+// static LDS is the prefill body's, as mixed_max_seqs assumes; checked once per kernel.
+static int check_static_lds(const void* kern, int D, const char* fn) {
+  static std::mutex mu;
+  static std::unordered_set<const void*> ok;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ok.count(kern)) return PA_OK;
+  hipFuncAttributes a;
+  if (hipFuncGetAttributes(&a, kern) != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: hipFuncGetAttributes failed", fn);
+  if (a.sharedSizeBytes != (size_t)prefill_lds_bytes(D))
+    return fail(PA_ERR_HIP, "%s: kernel holds %zu bytes of static LDS, expected %d", fn,
+                a.sharedSizeBytes, prefill_lds_bytes(D));
+  ok.insert(kern);
+  return PA_OK;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -127,8 +260,9 @@ using namespace pa;
 extern "C" size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t max_seqlen_k) {
-  if (num_seqs <= 0 || num_seqs > kMaxMixedSeqs || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads || head_dim <= 0 || max_seqlen_k <= 0)
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      (head_dim != 64 && head_dim != 128) || num_seqs > mixed_max_seqs(head_dim) ||
+      max_seqlen_k <= 0)
     return 0;
   return plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, PA_BF16, max_seqlen_k, 0, true)
       .ws_bytes;
@@ -159,8 +293,9 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   if ((int64_t)block_size * num_kv_heads * head_dim >= (int64_t)1 << 31)
     return fail(PA_ERR_UNSUPPORTED, "%s: block of %d x %d x %d elements too large", fn, block_size,
                 num_kv_heads, head_dim);
-  if (num_seqs > kMaxMixedSeqs)
-    return fail(PA_ERR_UNSUPPORTED, "%s: %d sequences (at most %d)", fn, num_seqs, kMaxMixedSeqs);
+  if (num_seqs > mixed_max_seqs(head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d sequences (at most %d at head_dim %d)", fn, num_seqs,
+                mixed_max_seqs(head_dim), head_dim);
   if ((int64_t)total_q > (int64_t)num_seqs * max_seqlen_q)
     return fail(PA_ERR_SHAPE, "%s: total_q %d > num_seqs * max_seqlen_q", fn, total_q);
   if (max_seqlen_q > max_seqlen_k)
@@ -190,31 +325,36 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   const bool wide = block_size >= kPrefillKeys;
   mixed_fn kern = dtype == PA_F16 ? pick_mixed<PA_F16>(head_dim, wide, G)
                                   : pick_mixed<PA_BF16>(head_dim, wide, G);
-  // Prefill workgroups: at most one per compute unit, each looping over the tile list;
-  // fewer when the batch cannot hold that many tiles (sum over prefill sequences of
-  // ceil(Lq / BM) <= total_q / BM + number of such sequences).
+  if (int st = check_static_lds(reinterpret_cast<const void*>(kern), head_dim, fn)) return st;
+  // Workgroups: up to one per compute unit.  The decode side has at most the balanced
+  // split's own count (its slices times head waves, 8 waves a workgroup); the prefill side
+  // at most one per tile the batch can hold (sum over prefill sequences of ceil(Lq / BM)
+  // <= total_q / BM + number of such sequences).  The kernel divides them.
   const int BM = kPrefillRows / G;
-  int64_t n_pf = 0;
+  int64_t pf_wgs = 0;
   if (max_seqlen_q > 1) {
     const int64_t seqs = num_seqs < total_q / 2 ? num_seqs : total_q / 2;
     int64_t tiles = total_q / BM + seqs;
     const int64_t by_len = (int64_t)num_seqs * ((max_seqlen_q + BM - 1) / BM);
     tiles = tiles < by_len ? tiles : by_len;
-    n_pf = tiles * num_kv_heads;
-    n_pf = n_pf < kNumCUs ? n_pf : kNumCUs;
+    pf_wgs = tiles * num_kv_heads;
+    pf_wgs = pf_wgs < kNumCUs ? pf_wgs : kNumCUs;
   }
-  const int head_waves = num_kv_heads * (G / head_tile(G));
-  const int64_t n_dec = ceil_div((int64_t)pl.Wt * head_waves, kPrefillThreads / 64);
-  if (n_pf + n_dec > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: grid too large", fn);
+  constexpr int kWaves = kPrefillThreads / 64;
+  const int head_waves = num_kv_heads * (G / mixed_head_tile(G));
+  // The balanced split's wave count (as pa_decode plans it), and at least one slice.
+  const int64_t dec_wgs = std::max(ceil_div((int64_t)pl.Wt * num_kv_heads * (G / pl.G), kWaves),
+                                   ceil_div(head_waves, kWaves));
+  const int64_t n_wg = dec_wgs + pf_wgs < kNumCUs ? dec_wgs + pf_wgs : kNumCUs;
+  if (dec_wgs > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: grid too large", fn);
   const WsPtrs w = carve(workspace, pl, num_seqs, num_q_heads, head_dim);
   const hipStream_t s = (hipStream_t)stream;
-  const size_t lds = (size_t)(3 * num_seqs + 1) * sizeof(int);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(n_pf + n_dec)), dim3(kPrefillThreads), lds, s,
+  hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(kPrefillThreads), mixed_dyn_lds(num_seqs), s,
                      (uint16_t*)out, (const uint16_t*)q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, block_table, max_blocks_per_seq, cu_seqlens_q,
                      cu_seqlens_k, total_q, num_seqs, num_blocks, __builtin_ctz(block_size),
-                     num_q_heads, num_kv_heads, scale * kLog2e, (int)n_pf, w.acc, w.m, w.l,
-                     w.cuc, head_waves, pl.Wt);
+                     num_q_heads, num_kv_heads, scale * kLog2e, w.acc, w.m, w.l, w.cuc,
+                     head_waves, pl.Wt, (int)dec_wgs);
   int st = check_launch(fn);
   if (st) return st;
   // Pieces per decode row: at most one more than the slices per sequence.

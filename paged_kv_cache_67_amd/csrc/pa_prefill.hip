@@ -40,9 +40,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(
   // tiles that read the same K/V rows hit the same L2.
   const int nx = gridDim.x, ny = gridDim.y;
   const int lid = xcd_local_id(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
-  prefill_body<D, G, WIDE, false, ET>(lid % nx, (lid / nx) % ny, lid / (nx * ny), out, q, kc, vc,
-                                  block_table, maxb, cu_q, cu_k, total_q, num_blocks, bs_log2, HQ,
-                                  HKV, scale_log2, causal);
+  prefill_body<D, G, WIDE, false, ET>(threadIdx.x, lid % nx, (lid / nx) % ny, lid / (nx * ny), out,
+                                      q, kc, vc, block_table, maxb, cu_q, cu_k, total_q,
+                                      num_blocks, bs_log2, HQ, HKV, scale_log2, causal);
 }
 
 typedef void (*prefill_fn)(uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,

@@ -19,6 +19,8 @@ constexpr int kPrefillKeys = 128;     // keys per tile
 constexpr int kPrefillThreads = 512;  // 8 waves: 4 row groups x 2 key halves
 constexpr int kBtCache = 2048;        // block-table entries of one sequence kept in LDS
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is moved
+// Static LDS of one prefill workgroup: four K/V tile buffers, the block-table window and a flag.
+constexpr int prefill_lds_bytes(int D) { return 4 * kPrefillKeys * D * 2 + kBtCache * 4 + 4; }
 // Running max before any unmasked key: finite, so that a masked score (-inf) still gives
 // exp2(-inf - m) = 0 rather than NaN, and a key half that never sees a key merges with weight 0.
 constexpr float kNoMax = -1.0e30f;
@@ -101,12 +103,14 @@ __device__ __forceinline__ float max_over_groups(float x) {
 // V_{t+1} straight into the two buffers step t - 1 finished reading, and it ends with a
 // wait for them and one barrier.  WIDE (block_size >= 128): every tile lies inside one
 // block, so a tile's address is a scalar base plus a per-lane offset.
-// The body of one workgroup item: query tile qt of sequence b for KV head g.  MIXED: the
+// The body of one workgroup item: query tile qt of sequence b for KV head g; tid is the
+// thread's index in the workgroup (threadIdx.x, passed in so that a caller looping over
+// items can keep the lane-dependent setup inside its loop).  MIXED: the
 // batch also holds decode rows (sequences with one query), which the decode side of the
 // launch handles; such a sequence is skipped here.
 template <int D, int G, bool WIDE, bool MIXED, int ET>
 __device__ __forceinline__ void prefill_body(
-    int qt, int g, int b, uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
+    int tid, int qt, int g, int b, uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int total_q, int num_blocks, int bs_log2, int HQ, int HKV,
@@ -131,8 +135,8 @@ __device__ __forceinline__ void prefill_body(
   __shared__ int s_bt[kBtCache];
   static_assert(kBtCache % NT == 0, "block-table window split over the threads");
   __shared__ int s_bad;
+  static_assert(sizeof(sKV) + sizeof(s_bt) + sizeof(s_bad) == prefill_lds_bytes(D), "LDS size");
 
-  const int tid = threadIdx.x;
   const int32_t* bt = block_table + (int64_t)b * maxb;
   // The first kBtCache block-table entries are fetched before the sequence lengths arrive
   // (they depend only on the sequence index), so the two loads overlap; they are checked

@@ -142,14 +142,42 @@ def test_workspace_size_closed_form(L):
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 256) == 0   # one partition: no workspace
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 16) == 2 * 2 * 3 * 66 * 4
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, -1) == 0    # single pass
-    # balanced: [HQ][W][2] states + (B+1) int32; W = 2048 waves / 8 KV-head waves
-    assert L.pa_decode_workspace_size(256, 16, 8, 128, 4096, 0) == 16 * 256 * 2 * 130 * 4 + 257 * 4
+    # balanced: [HQ][W][2] states + (B+2) int32.  A batch that may read more than 256 MiB
+    # of K/V (256 x 4096 keys x 8 heads x 128 x 2 x 2 bytes) is split over 1536 waves:
+    # W = 1536 / 8 KV-head waves
+    assert L.pa_decode_workspace_size(256, 16, 8, 128, 4096, 0) == 16 * 192 * 2 * 130 * 4 + 258 * 4
+    # one that fits the cache over 2048 waves (64 x 2007 x 2 x 64 x 2 x 2 bytes)
+    assert L.pa_decode_workspace_size(64, 14, 2, 64, 2007, 0) == 14 * 1024 * 2 * 66 * 4 + 66 * 4
     # W is capped by the number of chunks there can be (fp32 d64 chunk: 16 tokens)
-    assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 0) == 2 * 6 * 2 * 66 * 4 + 3 * 4
+    assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 0) == 2 * 6 * 2 * 66 * 4 + 4 * 4
     assert L.pa_decode_workspace_size(2, 3, 2, 64, 33, 0) == 0     # invalid head ratio
     # the mixed launch uses the balanced bf16 layout over all its sequences
-    assert L.pa_mixed_workspace_size(264, 16, 8, 128, 4096) == 16 * 256 * 2 * 130 * 4 + 265 * 4
+    assert L.pa_mixed_workspace_size(264, 16, 8, 128, 4096) == 16 * 192 * 2 * 130 * 4 + 266 * 4
     assert L.pa_mixed_workspace_size(5000, 16, 8, 128, 4096) == 0
+
+
+# The mixed launch's LDS: the prefill body's static tiles (1024 * head_dim bytes of K/V
+# buffers, 8 KiB of block-table window, one flag) plus (3 * num_seqs + 5) ints, within
+# 160 KiB: at most 2046 sequences at head_dim 128 and 7507 at head_dim 64.
+MIXED_MAX_SEQS = {128: 2046, 64: 7507}
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_mixed_sequence_limit(L, head_dim):
+    n = MIXED_MAX_SEQS[head_dim]
+    static = 4 * 128 * head_dim * 2 + 2048 * 4 + 4
+    assert static + (3 * n + 5) * 4 <= 160 * 1024 < static + (3 * (n + 1) + 5) * 4
+    assert L.pa_mixed_workspace_size(n, 16, 8, head_dim, 4096) > 0
+    assert L.pa_mixed_workspace_size(n + 1, 16, 8, head_dim, 4096) == 0
+    a = ctypes.c_void_p(0x10000)
+    # (out, q, k, v, bt, maxb, cu_q, cu_k, B, total_q, max_q, max_k, nblocks, bs, HQ, HKV, D,
+    #  scale, dtype, ws, ws_bytes, stream): at the bound the call gets as far as the missing
+    # workspace; one past it is refused for its size.  Nothing is launched.
+    assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, n, n, 1, 64, 8, 16, 16, 8, head_dim,
+                                0.1, 1, None, 0, None) == 5
+    assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, n + 1, n + 1, 1, 64, 8, 16, 16, 8,
+                                head_dim, 0.1, 1, None, 0, None) == 3
+    assert f"at most {n}" in pk.pa_last_error()
 
 
 def test_copy_blocks_validation(L):
