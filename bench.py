@@ -444,9 +444,82 @@ def _oracle_sample(w, kp, vp, gpu, seconds):
     return done, np.stack(errs), nbytes, wall, time.process_time() - cpu0
 
 
+def host_cpu():
+    """The host's CPU facts: os.cpu_count(), the CPUs this process may run on, the model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "affinity": affinity, "cpu_model": model}
+
+
+# Oracle worker processes share the parent's pools (fork, copy-on-write) and take whole
+# sequences; they are started from a child process that has not touched the GPU.
+_OW = {}
+
+
+def _oracle_seq(b):
+    import oracle
+    w, kp, vp = _OW["w"], _OW["kp"], _OW["vp"]
+    sl = slice(int(b), int(b) + 1)
+    slots = oracle.slot_mapping(w.block_table[sl], np.array([0, 1]), w.seq_lens_k[sl], w.block_size)
+    oracle.store_kv(kp, vp, w.k_new[sl], w.v_new[sl], slots)
+    oracle.decode(w.q[sl], kp, vp, w.block_table[sl], w.seq_lens_k[sl], w.scale, w.dtype)
+    kv, q, bt = decode_bytes_sample(w, int(b))
+    return kv + 2 * q + bt
+
+
+def _oracle_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        _OW["limit"] = threadpool_limits(limits=1)
+    except ImportError:
+        pass
+
+
+def oracle_all_cores(seconds, workers):
+    """Child-process leg: the oracle over the same batch's sequences (same random order) in
+    `workers` processes of one thread each for about `seconds`; prints one JSON line."""
+    import multiprocessing as mp
+
+    import oracle
+    from workloads import make_config
+    w = make_config(2)
+    kp, vp = w.empty_pool(), w.empty_pool()
+    oracle.store_kv(kp, vp, w.k_hist, w.v_hist,
+                    oracle.slot_mapping(w.block_table, w.cu_seqlens_hist, w.hist_lens, w.block_size))
+    _OW.update(w=w, kp=kp, vp=vp)
+    # the batch's sequences in the parent's random order, repeated so that the pool stays
+    # busy for the whole interval (a repeat rewrites the same rows and recomputes the rows)
+    order = [int(b) for b in np.random.default_rng(0).permutation(w.num_seqs)] * 200
+    done = nbytes = 0
+    with mp.get_context("fork").Pool(workers, initializer=_oracle_worker_init) as pool:
+        t0 = time.perf_counter()
+        for nb in pool.imap_unordered(_oracle_seq, order):
+            done += 1
+            nbytes += nb
+            if time.perf_counter() - t0 >= seconds:
+                break
+        wall = time.perf_counter() - t0
+        pool.terminate()
+    print(json.dumps({"done": done, "bytes": int(nbytes), "wall": wall}), flush=True)
+
+
 def cpu_baseline(w, dw, seconds):
-    """Time the CPU oracle on a bounded sample of the same batch (all host threads, and
-    again on one thread for a shorter sample); check the GPU rows on it too."""
+    """Time the CPU oracle on bounded samples of the same batch: in this process on one
+    thread (its outputs are compared with the GPU rows), then in a child process over one
+    single-thread worker per available CPU (at most 16)."""
+    import subprocess
+
     import oracle
     from paged_kv_cache_67_amd import harness
 
@@ -455,24 +528,111 @@ def cpu_baseline(w, dw, seconds):
     oracle.store_kv(kp, vp, w.k_hist, w.v_hist,
                     oracle.slot_mapping(w.block_table, w.cu_seqlens_hist, w.hist_lens, w.block_size))
     gpu = oracle.to_f64(harness.from_device(dw.out), w.dtype)
-    done, err, nbytes, wall, cpu = _oracle_sample(w, kp, vp, gpu, seconds)
-    log(f"cpu baseline: {len(done)} sequences in {wall:.1f} s; parity max {err.max():.2e} mean {err.mean():.2e}")
-    base = {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"{len(done)} of {w.num_seqs} sequences (random order, seed 0): slot mapping, "
-                      f"store and fp64 decode, {wall:.1f} s wall"}
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
-            d1, _, n1, wall1, _ = _oracle_sample(w, kp, vp, gpu, min(seconds, 5.0))
-        base["one_thread"] = {"value": round(n1 / wall1 / 1e9, 4), "unit": "GB/s", "cores": 1,
-                              "sample": f"first {len(d1)} sequences of the same order, {wall1:.1f} s wall"}
-        log(f"cpu baseline, one thread: {len(d1)} sequences in {wall1:.1f} s")
+            done, err, nbytes, wall, cpu = _oracle_sample(w, kp, vp, gpu, seconds)
     except ImportError:
-        pass
+        done, err, nbytes, wall, cpu = _oracle_sample(w, kp, vp, gpu, seconds)
+    log(f"cpu baseline, one thread: {len(done)} sequences in {wall:.1f} s; parity max "
+        f"{err.max():.2e} mean {err.mean():.2e}")
+    facts = host_cpu()
+    one = {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "sample": f"{len(done)} of {w.num_seqs} sequences (random order, seed 0): slot "
+                     f"mapping, store and fp64 decode, {wall:.1f} s wall",
+           "busy_ratio": round(cpu / wall, 2)}
+    workers = max(1, min(16, facts["affinity"] or 1))
+    base = None
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-leg",
+                        str(seconds), str(workers)], capture_output=True, text=True,
+                       timeout=seconds + 240)
+    if r.returncode == 0 and r.stdout.strip():
+        leg = json.loads(r.stdout.strip().splitlines()[-1])
+        log(f"cpu baseline, {workers} processes: {leg['done']} sequences in {leg['wall']:.1f} s")
+        base = {"value": round(leg["bytes"] / leg["wall"] / 1e9, 4), "unit": "GB/s",
+                "cores": workers, "kind": "oracle",
+                "sample": f"{leg['done']} sequence decodes (the batch's {w.num_seqs} in the same "
+                          f"order, repeated), {workers} single-thread processes, "
+                          f"{leg['wall']:.1f} s wall",
+                **facts, "threads_per_process": 1, "one_thread": one}
+    else:
+        log(f"cpu baseline: all-cores leg failed ({r.returncode}): {r.stderr[-500:]}")
+        base = {**one, "kind": "oracle", **facts, "note": "all-cores leg failed; one thread only"}
     return (base,
             {"sample_seqs": len(done), "max_err": float(err.max()), "mean_err": float(err.mean()),
              "ok": bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and np.all(np.isfinite(gpu)))})
+
+
+def time_ceiling(args):
+    """Read ceiling of the decode pass: pa_read_ceiling over two pools of 4096 blocks in the
+    decode's layout (block 256 x 8 KV heads x 128, bf16: 512 KiB per block and pool, 4 GiB in
+    all, 16 times the last-level cache), blocks in random order (the decode's pattern) and in
+    address order, at several grid sizes; median of 5 rounds of 10 launches between events."""
+    import torch
+
+    import paged_kv_cache_67_amd as pk
+
+    nb, bs, hkv, d = 4096, 256, 8, 128
+    kc = torch.empty((nb, bs, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    kc.view(torch.int16).random_()
+    vc.view(torch.int16).random_()
+    nbytes = 2 * kc.numel() * kc.element_size()
+    orders = {"random_blocks": torch.from_numpy(
+        np.random.default_rng(67009).permutation(nb).astype(np.int32)).cuda(),
+        "address_order": torch.arange(nb, dtype=torch.int32, device="cuda")}
+    res = {"bytes_per_launch": nbytes}
+    for name, ids in orders.items():
+        by = {}
+        for grid in (128, 192, 256, 512, 1024):
+            sink = torch.empty(8 * grid, dtype=torch.int32, device="cuda")
+            for _ in range(2):
+                pk.pa_read_ceiling(kc, vc, ids, grid, sink)
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    pk.pa_read_ceiling(kc, vc, ids, grid, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3 / 10)
+            us = float(np.median(per))
+            by[str(grid)] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        best = max(by, key=lambda k: by[k])
+        res[name] = {"GBps": by[best], "grid": int(best), "by_grid_GBps": by}
+        log(f"read ceiling ({name}): {by[best]:.0f} GB/s at {best} workgroups; {by}")
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_tp_shard(args):
+    """One TP=2 rank's share of the decode batch (8 Q / 4 KV heads, the same contexts):
+    pa_decode (both passes) by HIP graph replay."""
+    import torch
+
+    from paged_kv_cache_67_amd import harness
+    from workloads import make_tp_shard
+
+    w = make_tp_shard(2)
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    dw.slot_mapping()
+    dw.store()
+    torch.cuda.synchronize()
+    kv, q, bt = decode_bytes(w)
+    nbytes = kv + 2 * q + bt
+    us = _graph_us(dw.attention, max(20, args.steps // 5))
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"{w.name}: pa_decode {us:.1f} us, {gbs:.1f} GB/s")
+    del dw
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes), "GBps": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": "HIP graph of one pa_decode, replayed between two events"}
 
 
 PROFILE = os.path.join(ROOT, "profiles", "decode_qwen3-0.6b-b256.md")
@@ -539,7 +699,14 @@ def main():
                     help="finish with 3 x 1 GiB device copies (counter calibration runs)")
     ap.add_argument("--partition", type=int, default=0,
                     help="decode split: 0 balanced (default), -1 single pass, P fixed partitions")
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-tp-shard", action="store_true")
+    ap.add_argument("--oracle-leg", nargs=2, metavar=("SECONDS", "WORKERS"),
+                    help=argparse.SUPPRESS)  # internal: the all-cores oracle leg (no GPU)
     args = ap.parse_args()
+    if args.oracle_leg:
+        oracle_all_cores(float(args.oracle_leg[0]), int(args.oracle_leg[1]))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the paged-attention path needs no collective and this "
               "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
@@ -607,6 +774,13 @@ def main():
     else:
         result["cpu_baseline"] = None
     extra = {}
+    if not args.no_ceiling:
+        ceil = time_ceiling(args)
+        extra["read_ceiling"] = ceil
+        c = ceil["random_blocks"]["GBps"]
+        result["roofline"]["ceiling"] = {
+            "GBps": c, "kind": "pa_read_ceiling: the decode's loads over random 512 KiB blocks",
+            "frac": round(achieved / c, 4)}
     if not args.no_f16:
         extra["f16_decode"] = time_f16_decode(w, dw, args)
     if not args.no_graphs:
@@ -622,6 +796,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_mixed:
         extra["mixed"] = time_mixed(args)
+        torch.cuda.empty_cache()
+    if not args.no_tp_shard:
+        extra["tp2_rank"] = time_tp_shard(args)
     if extra:
         result["extra"] = extra
     if args.copy_calibration:

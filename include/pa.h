@@ -302,10 +302,12 @@ int pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* 
 /*
  * pa_mixed_workspace_size -- bytes of workspace pa_attention_mixed needs.
  *
- * For num_seqs sequences (at most 4096) whose key counts are at most
- * max_seqlen_k; 0 for invalid sizes.  The layout is the balanced split's of
- * pa_decode (per query head and slice two partial states, then the chunk
- * prefix sums), covering the batch's decode rows.
+ * For num_seqs sequences whose key counts are at most max_seqlen_k; 0 for
+ * invalid sizes, including head_dim other than 64 and 128 and more sequences
+ * than pa_attention_mixed takes (2046 at head_dim 128, 7507 at head_dim 64).
+ * The layout is the balanced split's of pa_decode (per query head and slice
+ * two partial states, then the chunk prefix sums and the slice count the
+ * launch used), covering the batch's decode rows.
  */
 size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t max_seqlen_k);
@@ -321,15 +323,23 @@ size_t pa_mixed_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t nu
  * with Lq = 1 is a decode row ([mini] section 5: its one query attends all Lk
  * keys); such rows take the split-K decode path and the others the matrix-core
  * prefill path, inside the same launch, followed by a small merge launch on
- * the same stream.  A decode row with Lk = 0 gives a zero row.
+ * the same stream.  A decode row with Lk = 0 gives a zero row.  The launch
+ * holds at most one workgroup per compute unit; each workgroup scans the
+ * lengths and, with the same arithmetic in all of them, divides the
+ * workgroups between the two sides so that the HBM-bound decode rows and the
+ * matrix-bound prefill tiles run side by side.
  *
  *   workspace    scratch of pa_mixed_workspace_size(num_seqs, num_q_heads,
  *                num_kv_heads, head_dim, max_seqlen_k) bytes, 16-byte aligned,
  *                owned by the caller; no initialisation needed
  *
- * dtype must be PA_BF16 or PA_F16, scale > 0, num_seqs <= 4096, num_q_heads/num_kv_heads
- * in 1..8 or 16.  Errors as for pa_prefill_paged, plus PA_ERR_WORKSPACE for a
- * missing or short workspace.
+ * dtype must be PA_BF16 or PA_F16, scale > 0, num_q_heads/num_kv_heads in
+ * 1..8 or 16.  num_seqs is bounded by the workgroup's LDS (160 KiB): the
+ * prefill tiles hold 1024 * head_dim + 8196 bytes and the length scan
+ * (3 * num_seqs + 5) * 4 bytes, so at most 2046 sequences at head_dim 128 and
+ * 7507 at head_dim 64; a larger batch is refused with PA_ERR_UNSUPPORTED.
+ * Errors as for pa_prefill_paged, plus PA_ERR_WORKSPACE for a missing or
+ * short workspace.
  */
 int pa_attention_mixed(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -356,6 +366,34 @@ int pa_attention_mixed(void* out, const void* q, const void* k_cache, const void
 int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
                    int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                    int32_t head_dim, pa_dtype dtype, void* stream);
+
+/*
+ * pa_read_ceiling -- measurement helper: the read bandwidth the decode pass
+ * can reach.  Not part of the attention path.
+ *
+ * Reads every K and V byte of the pool blocks block_ids[0 .. num_ids) once
+ * ([KVblog] 3.1: a block holds block_size rows of [num_kv_heads][head_dim])
+ * with the decode's loads and wave-to-data mapping (one wave per KV head
+ * reading that head's slice of each row, 16 bytes per lane, non-temporal) and
+ * no arithmetic, and XORs what it read into sink so that no load is dropped.
+ * Timing it over a pool larger than the last-level cache gives the ceiling the
+ * decode pass is measured against.
+ *
+ *   block_ids      in   DEVICE int32 [num_ids]; ids outside [0, num_blocks)
+ *                       are skipped
+ *   num_workgroups      grid size (512 threads each), > 0
+ *   sink           out  DEVICE uint32 [num_workgroups * 8], 4-byte aligned: the
+ *                       XOR of the 32-bit words each wave read (the XOR of all
+ *                       entries is the XOR of every word of the listed blocks,
+ *                       a block listed twice cancelling)
+ *
+ * Errors: PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (head_dim, block_size, dtype as for
+ * the caches), PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_HIP.
+ */
+int pa_read_ceiling(const void* k_cache, const void* v_cache, const int32_t* block_ids,
+                    int32_t num_ids, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                    int32_t num_workgroups, uint32_t* sink, void* stream);
 
 /*
  * Debug checks of the device-side contract stated at the top of this file.

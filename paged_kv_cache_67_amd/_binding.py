@@ -47,6 +47,8 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp, _sz,
                                      _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_read_ceiling": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _i32,
+                                  _vp, _vp]),
     "pa_set_debug_checks": (C.c_int, [C.c_int]),
     "pa_check_store_inputs": (C.c_int, [_vp, _i32, _i32, _i32, _vp]),
     "pa_check_decode_inputs": (C.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
@@ -311,6 +313,19 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
     _check("pa_copy_blocks", lib().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0], NB, BS, HKV, D,
         _dtype(k_cache), _stream(stream)))
+
+
+def pa_read_ceiling(k_cache, v_cache, block_ids, num_workgroups, sink, stream=None):
+    """Read every K/V byte of the listed pool blocks once (the decode's loads, no arithmetic);
+    sink: device uint32 [num_workgroups * 8] receives the XOR of what each wave read."""
+    NB, BS, HKV, D = k_cache.shape
+    assert v_cache.shape == k_cache.shape and k_cache.is_contiguous() and v_cache.is_contiguous()
+    assert v_cache.dtype == k_cache.dtype
+    assert block_ids.dtype == torch.int32 and block_ids.is_contiguous() and block_ids.dim() == 1
+    assert sink.dtype in (torch.int32, torch.uint32) and sink.numel() >= 8 * num_workgroups
+    _check("pa_read_ceiling", lib().pa_read_ceiling(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_ids), block_ids.numel(), NB, BS, HKV, D,
+        _dtype(k_cache), int(num_workgroups), _ptr(sink), _stream(stream)))
 
 
 def _host_i32(values):

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["pa_status.cpp", "pa_blocks.cpp", "pa_check.cpp", "pa_store.hip", "pa_decode.hip",
-           "pa_prefill.hip", "pa_mixed.hip"]
+           "pa_prefill.hip", "pa_mixed.hip", "pa_ceiling.hip"]
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 

@@ -44,13 +44,18 @@ inline DecodePlan plan_decode(int32_t B, int32_t HQ, int32_t HKV, int32_t D, pa_
     const double kv_bytes = (double)B * (max_ctx > 0 ? max_ctx : 1) * HKV * D * elt_bytes(dtype) * 2;
     const int slots =
         kv_bytes > (double)kInfinityCacheBytes ? PA_DECODE_WAVE_SLOTS_HBM : PA_DECODE_WAVE_SLOTS;
-    int64_t Wt = (int64_t)slots / head_waves;
-    Wt = Wt < 1 ? 1 : Wt;
     const int64_t max_chunks = (int64_t)B * ceil_div(max_ctx > 0 ? max_ctx : 1, CH);
-    if (Wt > max_chunks) Wt = max_chunks;
-    pl.Wt = (int)Wt;
-    const size_t states = (size_t)HQ * pl.Wt * 2;
-    // States, then the chunk scan s_cuc [B + 1] and the slice count the first pass used.
+    auto slices = [&](int64_t waves) {
+      const int64_t w = waves / head_waves;
+      return w < 1 ? 1 : (w > max_chunks ? max_chunks : w);
+    };
+    pl.Wt = (int)slices(slots);
+    // The workspace covers the larger wave count whichever is used, so that its size never
+    // shrinks as the batch grows (a buffer sized for the largest batch serves every smaller
+    // one): states, then the chunk scan s_cuc [B + 1] and the slice count of a mixed launch.
+    const int64_t Wmax = slices(PA_DECODE_WAVE_SLOTS > PA_DECODE_WAVE_SLOTS_HBM
+                                    ? PA_DECODE_WAVE_SLOTS : PA_DECODE_WAVE_SLOTS_HBM);
+    const size_t states = (size_t)HQ * Wmax * 2;
     pl.ws_bytes = states * (D + 2) * sizeof(float) + (size_t)(B + 2) * sizeof(int32_t);
   } else {
     pl.P = partition_size > 0 ? partition_size : auto_partition(B, HKV, max_ctx);

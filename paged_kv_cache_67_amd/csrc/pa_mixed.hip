@@ -20,9 +20,9 @@
 // reach its bandwidth on about 160-192 compute units; the prefill tiles are bound by the
 // matrix cores and LDS of their own compute unit and read little, so the two sides run
 // side by side and the step takes about the longer of the two instead of their sum.  The
-// split minimises the larger of the two modelled times (decode bytes over the bandwidth
-// of its workgroups, rounds of prefill tiles times the mean tile's flops over a
-// workgroup's rate).  Decode rows cut by slice boundaries leave partial states in the
+// split minimises the larger of the two modelled times (decode bytes over the measured
+// bandwidth of that many workgroups, rounds of prefill tiles times the mean tile's flops
+// over a workgroup's rate).  Decode rows cut by slice boundaries leave partial states in the
 // workspace; a second small launch merges them.
 #include <algorithm>
 #include <mutex>
@@ -33,12 +33,28 @@
 
 namespace pa {
 
-// Rates of the split's cost model, measured on MI355X: decode K/V bytes per ns of one
-// decode workgroup (eight waves) and of the whole chip, and flops per ns of one prefill
-// workgroup.
-constexpr float kDecBytesPerNsWG = 40.0f;
-constexpr float kDecBytesPerNsChip = 6500.0f;
+// Rates of the split's cost model, measured on MI355X with the 256-row Qwen3-0.6B decode
+// batch beside 8 prompt chunks and a fixed number of decode workgroups: decode K/V bytes
+// per ns reached by n decode workgroups (eight waves each; linear between the points,
+// flat past the last), taken at 90% while prefill tiles run beside them (the heavier
+// mixes measured so); and flops per ns of one prefill workgroup (the prefill kernel's
+// 540 TFLOP/s over 256 workgroups).
+constexpr int kDecCurveN = 7;
+__device__ constexpr float kDecCurveWGs[kDecCurveN] = {0, 96, 128, 144, 160, 176, 192};
+__device__ constexpr float kDecCurveBytesPerNs[kDecCurveN] = {0, 4530, 5540, 5900, 6210, 6360, 6450};
+constexpr float kDecBesidePrefill = 0.9f;
 constexpr float kPfFlopsPerNsWG = 2100.0f;
+
+__device__ __forceinline__ float decode_bytes_per_ns(float n) {
+  float r = kDecCurveBytesPerNs[kDecCurveN - 1];
+#pragma unroll
+  for (int k = kDecCurveN - 1; k >= 1; --k)
+    if (n <= kDecCurveWGs[k])
+      r = kDecCurveBytesPerNs[k - 1] + (n - kDecCurveWGs[k - 1]) *
+                                           (kDecCurveBytesPerNs[k] - kDecCurveBytesPerNs[k - 1]) /
+                                           (kDecCurveWGs[k] - kDecCurveWGs[k - 1]);
+  return kDecBesidePrefill * r;
+}
 
 constexpr int kMaxLdsBytes = 160 * 1024;  // LDS one workgroup may hold (gfx950)
 // Dynamic LDS of a mixed workgroup: the split (4 ints), then the decode tables
@@ -114,7 +130,7 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
       int best_n = lo;
       for (int c = (lo + step - 1) / step * step + lane * step; c <= hi; c += 64 * step) {
         const int nd = min(n_wg - c, dec_wgs_max);
-        const float t_dec = dec_bytes / fminf(kDecBytesPerNsChip, (float)nd * kDecBytesPerNsWG);
+        const float t_dec = dec_bytes / decode_bytes_per_ns((float)nd);
         const float t_pf = (float)((items + c - 1) / c) * tile_ns;
         const float t = fmaxf(t_dec, t_pf);
         if (t < best_t) {

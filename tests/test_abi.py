@@ -142,17 +142,18 @@ def test_workspace_size_closed_form(L):
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 256) == 0   # one partition: no workspace
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 16) == 2 * 2 * 3 * 66 * 4
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, -1) == 0    # single pass
-    # balanced: [HQ][W][2] states + (B+2) int32.  A batch that may read more than 256 MiB
-    # of K/V (256 x 4096 keys x 8 heads x 128 x 2 x 2 bytes) is split over 1536 waves:
-    # W = 1536 / 8 KV-head waves
-    assert L.pa_decode_workspace_size(256, 16, 8, 128, 4096, 0) == 16 * 192 * 2 * 130 * 4 + 258 * 4
-    # one that fits the cache over 2048 waves (64 x 2007 x 2 x 64 x 2 x 2 bytes)
+    # balanced: [HQ][W][2] states + (B+2) int32, W = 2048 waves / 8 KV-head waves.  A batch
+    # that may read more than 256 MiB of K/V is split over 1536 waves only, but the
+    # workspace still covers 2048, so that it never shrinks as the batch grows
+    assert L.pa_decode_workspace_size(256, 16, 8, 128, 4096, 0) == 16 * 256 * 2 * 130 * 4 + 258 * 4
     assert L.pa_decode_workspace_size(64, 14, 2, 64, 2007, 0) == 14 * 1024 * 2 * 66 * 4 + 66 * 4
+    sizes = [L.pa_decode_workspace_size(b, 16, 8, 128, 4096, 0) for b in (1, 8, 32, 64, 65, 256, 4096)]
+    assert sizes == sorted(sizes)
     # W is capped by the number of chunks there can be (fp32 d64 chunk: 16 tokens)
     assert L.pa_decode_workspace_size(2, 2, 1, 64, 33, 0) == 2 * 6 * 2 * 66 * 4 + 4 * 4
     assert L.pa_decode_workspace_size(2, 3, 2, 64, 33, 0) == 0     # invalid head ratio
     # the mixed launch uses the balanced bf16 layout over all its sequences
-    assert L.pa_mixed_workspace_size(264, 16, 8, 128, 4096) == 16 * 192 * 2 * 130 * 4 + 266 * 4
+    assert L.pa_mixed_workspace_size(264, 16, 8, 128, 4096) == 16 * 256 * 2 * 130 * 4 + 266 * 4
     assert L.pa_mixed_workspace_size(5000, 16, 8, 128, 4096) == 0
 
 
@@ -178,6 +179,18 @@ def test_mixed_sequence_limit(L, head_dim):
     assert L.pa_attention_mixed(a, a, a, a, a, 4, a, a, n + 1, n + 1, 1, 64, 8, 16, 16, 8,
                                 head_dim, 0.1, 1, None, 0, None) == 3
     assert f"at most {n}" in pk.pa_last_error()
+
+
+def test_read_ceiling_validation(L):
+    a = ctypes.c_void_p(0x10000)
+    # (k, v, ids, num_ids, num_blocks, block_size, kv_heads, head_dim, dtype, workgroups, sink, stream)
+    assert L.pa_read_ceiling(a, a, a, -1, 8, 16, 2, 64, 1, 8, a, None) == 2
+    assert L.pa_read_ceiling(a, a, a, 4, 8, 16, 2, 64, 1, 0, a, None) == 2
+    assert L.pa_read_ceiling(a, a, a, 4, 8, 16, 2, 96, 1, 8, a, None) == 3
+    assert L.pa_read_ceiling(a, a, a, 4, 8, 12, 2, 64, 1, 8, a, None) == 3
+    assert L.pa_read_ceiling(a, a, a, 4, 8, 16, 2, 64, 7, 8, a, None) == 3
+    assert L.pa_read_ceiling(a, a, None, 4, 8, 16, 2, 64, 1, 8, a, None) == 1
+    assert L.pa_read_ceiling(a, a, a, 4, 8, 16, 2, 64, 1, 8, ctypes.c_void_p(0x10002), None) == 4
 
 
 def test_copy_blocks_validation(L):

@@ -16,6 +16,7 @@ from .synth import (  # noqa: F401
     bf16_bits_from_f32,
     make_config,
     make_mixed,
+    make_tp_shard,
     make_workload,
     nan_bits,
     normal_values,

@@ -261,6 +261,19 @@ def _c4(seed):
 CONFIGS = {0: _c0, 1: _c1, 2: _c2, 3: _c3, 4: _c4}
 
 
+def make_tp_shard(tp: int = 2, seed: int = 67002) -> Workload:
+    """One tensor-parallel rank's share of the 256-row Qwen3-0.6B decode batch: the same
+    context lengths (seed 67002), with the 16 Q / 8 KV heads split over tp ranks (each rank
+    holds whole KV heads and their query groups)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(128, 4096, size=256, endpoint=True).astype(np.int32)
+    return make_workload(
+        name=f"qwen3-0.6b-decode-b256-tp{tp}-rank", kind="decode", dtype="bf16",
+        num_q_heads=16 // tp, num_kv_heads=8 // tp, head_dim=128, block_size=256,
+        seq_lens_k=lens, pool_factor=1.25, max_blocks_per_seq=16,
+        scale=1.0 / math.sqrt(128), seed=seed, rng=rng)
+
+
 def make_mixed(seed: int = 67005, num_decode: int = 256, num_prefill: int = 8) -> Workload:
     """A serving step that mixes both kinds of rows (Qwen3-0.6B heads, block 256):
     ``num_decode`` decode rows (one query each, contexts uniform in [128, 4096]) followed
