@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
     } else {
       // Candidates: n_pf in [lo, hi], multiples of 8 on a full chip (each XCD then holds
       // the same share of both sides); each lane prices some, the cheapest wins (ties to
-      // fewer prefill workgroups).
+      // more prefill workgroups: equal modelled rounds of tiles run shorter on more of them).
       const int min_dec = (head_waves + WAVES - 1) / WAVES;
       const int lo = max(1, n_wg - dec_wgs_max), hi = n_wg - min_dec;
       const int step = n_wg >= 64 ? 8 : 1;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
         const float t_dec = dec_bytes / decode_bytes_per_ns((float)nd);
         const float t_pf = (float)((items + c - 1) / c) * tile_ns;
         const float t = fmaxf(t_dec, t_pf);
-        if (t < best_t) {
+        if (t <= best_t) {
           best_t = t;
           best_n = c;
         }
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kPrefillThreads) void mixed_kernel(
       for (int o = 32; o >= 1; o >>= 1) {
         const float ot = __shfl_xor(best_t, o);
         const int on = __shfl_xor(best_n, o);
-        if (ot < best_t || (ot == best_t && on < best_n)) {
+        if (ot < best_t || (ot == best_t && on > best_n)) {
           best_t = ot;
           best_n = on;
         }
