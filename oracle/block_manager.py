@@ -15,6 +15,13 @@ Sources (web pages; cited by the short name in brackets):
              (txtmix.com), "前缀缓存真正生效的条件" (three live sequences sharing two
              blocks).
 
+The pages print the allocate / may_append / deallocate code of nano-vllm; this file is
+written from the behaviour they describe instead, in its own structure: admission first
+finds the longest run of cached blocks at the front of the prompt, then claims those
+(share or take back), then hands out fresh blocks for the rest, then makes every full
+block findable.  Only the fingerprint (compute_hash) must match the pages' definition
+byte for byte.
+
 Readings where the pages leave a step open:
 
 * The hit test asks that the block the table names still carries this fingerprint and
@@ -43,7 +50,8 @@ memberships, free and used blocks partition the pool) over random operation sequ
 
 from __future__ import annotations
 
-from collections import deque
+import itertools
+from collections import OrderedDict
 
 import numpy as np
 import xxhash
@@ -64,170 +72,182 @@ def compute_hash(token_ids, prefix=None) -> int:
     return h.intdigest()
 
 
-class Block:
-    def __init__(self, block_id):
-        self.block_id = block_id
-        self.ref_count = 0
-        self.hash = None  # None: not a registered full block
-        self.token_ids = []
+class _Seq:
+    """A live sequence: its token ids, its block table and how many of its prompt tokens
+    were found in the cache at admission."""
 
-    def reset(self):
-        """A block handed to a sequence: the allocation is its first reference."""
-        self.ref_count = 1
-        self.hash = None
-        self.token_ids = []
-
-    def update(self, h, token_ids):
-        self.hash = h
-        self.token_ids = list(token_ids)
-
-
-class Sequence:
-    def __init__(self, token_ids):
-        self.token_ids = list(token_ids)
-        self.block_table = []
-        self.num_cached_tokens = 0
+    def __init__(self, tokens, table, cached):
+        self.tokens = tokens
+        self.table = table
+        self.cached = cached
 
 
 class BlockManager:
+    """The block pool of one KV cache and its prefix index.
+
+    State, per block: a reference count (how many live block tables hold it) and, for a
+    full block made findable, what it holds (fingerprint, token ids).  Free blocks (count
+    0) wait in an ordered set, least recently freed first; they keep what they hold until
+    they are handed out again, so a later prompt with the same prefix can take them back
+    (lazy reclamation, [KVblog] 3.4).  The index maps a fingerprint to the block that was
+    last made findable under it.
+    """
+
     def __init__(self, num_blocks, block_size):
         assert num_blocks >= 1 and block_size >= 2
+        self.num_blocks = num_blocks
         self.block_size = block_size
-        self.blocks = [Block(i) for i in range(num_blocks)]
-        self.hash_to_block_id = {}
-        self.free_block_ids = deque(range(num_blocks))
-        self.used_block_ids = set()
-        self.seqs = {}
-        self._next = 0
+        self._refs = [0] * num_blocks
+        self._holds = [None] * num_blocks           # (fingerprint, tokens) or None
+        self._free = OrderedDict.fromkeys(range(num_blocks))
+        self._index = {}                            # fingerprint -> block id
+        self._seqs = {}
+        self._handles = itertools.count()
 
-    # -- the block of logical index i of a sequence
-    def _block_tokens(self, seq, i):
-        return seq.token_ids[i * self.block_size:(i + 1) * self.block_size]
+    # -- helpers on token lists
+    def _chunk(self, tokens, i):
+        return tuple(tokens[i * self.block_size:(i + 1) * self.block_size])
 
-    def _num_blocks(self, n):
-        return (n + self.block_size - 1) // self.block_size
+    def _fingerprints(self, tokens):
+        """Chain fingerprints of the full blocks of a token list, first block first."""
+        fps, prev = [], None
+        for i in range(len(tokens) // self.block_size):
+            prev = compute_hash(self._chunk(tokens, i), prev)
+            fps.append(prev)
+        return fps
 
-    def _allocate_block(self, block_id):
-        block = self.blocks[block_id]
-        if block.hash is not None and self.hash_to_block_id.get(block.hash) == block_id:
-            del self.hash_to_block_id[block.hash]  # [Lab] B.6: the old mapping goes
-        block.reset()
-        self.free_block_ids.remove(block_id)
-        self.used_block_ids.add(block_id)
-        return block
+    # -- moves of single blocks
+    def _fresh(self):
+        """The least recently freed block, emptied for new contents: what it held is
+        forgotten, and its fingerprint leaves the index if the index still names it
+        ([Lab] B.6).  The caller's table is its first reference."""
+        b, _ = self._free.popitem(last=False)
+        held = self._holds[b]
+        if held is not None and self._index.get(held[0]) == b:
+            del self._index[held[0]]
+        self._holds[b] = None
+        self._refs[b] = 1
+        return b
 
-    def _deallocate_block(self, block_id):
-        assert self.blocks[block_id].ref_count == 0
-        self.used_block_ids.remove(block_id)
-        self.free_block_ids.append(block_id)  # keeps hash and tokens (lazy reclamation)
+    def _findable(self, b, fp, tokens):
+        self._holds[b] = (fp, tokens)
+        self._index[fp] = b
 
-    def can_allocate(self, n):
-        return len(self.free_block_ids) >= self._num_blocks(n)
+    def _lookup(self, fp, tokens):
+        """The block that still holds exactly these tokens under this fingerprint, if any
+        ([KVblog] 3.4: a fingerprint match with other tokens is no match)."""
+        b = self._index.get(fp)
+        if b is not None and self._holds[b] == (fp, tokens):
+            return b
+        return None
 
+    def _unref(self, b):
+        self._refs[b] -= 1
+        if self._refs[b] == 0:
+            self._free[b] = None  # joins the back of the free set, contents kept
+
+    # -- operations
     def allocate(self, token_ids):
-        """Admit a prompt: [KVblog] 3.3.3 (three paths, the first miss ends the hits)."""
-        if not token_ids:
+        """Admit a prompt ([KVblog] 3.3, 3.4; [Lab] B.6): its blocks are matched against
+        the cache from the first one on, and the first block without a match ends the
+        matching (a fingerprint stands for its whole prefix, so nothing after a miss can
+        be a valid hit); the prompt's last block is never matched, so at least its tokens
+        are computed.  A matched block in use by another sequence is shared (ALLOCATE's
+        REUSE outcome), a matched block that was freed is taken back (REACTIVATE), every
+        other block is fresh (ALLOCATE).  All full blocks of the prompt end up findable
+        under their fingerprints."""
+        tokens = [int(t) for t in token_ids]
+        if not tokens:
             raise ValueError("empty prompt")
-        if not self.can_allocate(len(token_ids)):
-            raise CapacityError(f"{self._num_blocks(len(token_ids))} blocks needed, "
-                                f"{len(self.free_block_ids)} free")
-        seq = Sequence(token_ids)
-        nb = self._num_blocks(len(token_ids))
-        h = None
-        cache_miss = False
-        for i in range(nb):
-            tokens = self._block_tokens(seq, i)
-            full = len(tokens) == self.block_size
-            h = compute_hash(tokens, h) if full else None
-            block_id = -1
-            if full and i < nb - 1:  # [Lab] B.6: the last block is not looked up
-                cand = self.hash_to_block_id.get(h, -1)
-                if cand >= 0 and self.blocks[cand].hash == h and \
-                        self.blocks[cand].token_ids == tokens:
-                    block_id = cand
-            if block_id < 0:
-                cache_miss = True
-            if cache_miss:  # ALLOCATE
-                block = self._allocate_block(self.free_block_ids[0])
+        need = -(-len(tokens) // self.block_size)
+        if len(self._free) < need:
+            raise CapacityError(f"{need} blocks needed, {len(self._free)} free")
+        fps = self._fingerprints(tokens)
+        matched = []
+        for i in range(min(len(fps), need - 1)):
+            b = self._lookup(fps[i], self._chunk(tokens, i))
+            if b is None:
+                break
+            matched.append(b)
+        table = []
+        for b in matched:
+            if self._refs[b] > 0:
+                self._refs[b] += 1  # shared with a live sequence
             else:
-                seq.num_cached_tokens += self.block_size
-                if block_id in self.used_block_ids:  # REUSE
-                    block = self.blocks[block_id]
-                    block.ref_count += 1
-                else:  # REACTIVATE
-                    block = self._allocate_block(block_id)
-            if full:
-                block.update(h, tokens)
-                self.hash_to_block_id[h] = block.block_id
-            seq.block_table.append(block.block_id)
-        sid = self._next
-        self._next += 1
-        self.seqs[sid] = seq
-        return sid
+                del self._free[b]  # freed but intact: back in use
+                self._refs[b] = 1
+            table.append(b)
+        table += [self._fresh() for _ in range(need - len(matched))]
+        for i, fp in enumerate(fps):
+            self._findable(table[i], fp, self._chunk(tokens, i))
+        handle = next(self._handles)
+        self._seqs[handle] = _Seq(tokens, table, len(matched) * self.block_size)
+        return handle
 
-    def append(self, sid, token_id):
-        """One generated token ([KVblog] 3.3.4, with copy-on-write from 2.2).  Returns
-        the (src, dst) pair to copy on the device, or None."""
-        seq = self.seqs[sid]
-        seq.token_ids.append(int(token_id))
-        n = len(seq.token_ids)
+    def append(self, handle, token_id):
+        """One generated token ([KVblog] 3.3, 2.2).  A token that starts a block gets a
+        fresh block; a token written into a last block that other sequences share first
+        moves this sequence to a fresh copy of it, and (source, copy) is returned for the
+        caller to copy the K/V rows on the device (else None).  A token that completes a
+        block makes it findable."""
+        s = self._seqs[handle]
+        n = len(s.tokens) + 1
         cow = None
-        if n % self.block_size == 1:  # the token opens a new block
-            if not self.free_block_ids:
-                seq.token_ids.pop()
+        if n % self.block_size == 1:  # the token starts a block
+            if not self._free:
                 raise CapacityError("no free block")
-            block = self._allocate_block(self.free_block_ids[0])
-            seq.block_table.append(block.block_id)
-        elif self.blocks[seq.block_table[-1]].ref_count > 1:  # shared: copy on write
-            if not self.free_block_ids:
-                seq.token_ids.pop()
+            s.table.append(self._fresh())
+        elif self._refs[s.table[-1]] > 1:  # shared last block: copy on write
+            if not self._free:
                 raise CapacityError("no free block")
-            src = seq.block_table[-1]
-            block = self._allocate_block(self.free_block_ids[0])
-            self.blocks[src].ref_count -= 1
-            seq.block_table[-1] = block.block_id
-            cow = (src, block.block_id)
-        if n % self.block_size == 0:  # the token fills its block: register it
+            src = s.table[-1]
+            s.table[-1] = self._fresh()
+            self._refs[src] -= 1  # others still hold it
+            cow = (src, s.table[-1])
+        s.tokens.append(int(token_id))
+        if n % self.block_size == 0:  # the token completes its block
             i = n // self.block_size - 1
-            tokens = self._block_tokens(seq, i)
-            prefix = self.blocks[seq.block_table[i - 1]].hash if i > 0 else None
-            h = compute_hash(tokens, prefix)
-            self.blocks[seq.block_table[i]].update(h, tokens)
-            self.hash_to_block_id[h] = seq.block_table[i]
+            self._findable(s.table[i], self._fingerprints(s.tokens)[i], self._chunk(s.tokens, i))
         return cow
 
-    def fork(self, sid):
-        parent = self.seqs[sid]
-        child = Sequence(parent.token_ids)
-        child.block_table = list(parent.block_table)
-        child.num_cached_tokens = parent.num_cached_tokens
-        for b in child.block_table:
-            self.blocks[b].ref_count += 1
-        cid = self._next
-        self._next += 1
-        self.seqs[cid] = child
-        return cid
+    def fork(self, handle):
+        """A new sequence with the same tokens sharing every block (one more reference
+        each); the first token either writes into a shared block copies it."""
+        s = self._seqs[handle]
+        for b in s.table:
+            self._refs[b] += 1
+        child = next(self._handles)
+        self._seqs[child] = _Seq(list(s.tokens), list(s.table), s.cached)
+        return child
 
-    def free(self, sid):
-        """[KVblog] 3.3.5: one reference less per block, last block first."""
-        seq = self.seqs.pop(sid)
-        for b in reversed(seq.block_table):
-            self.blocks[b].ref_count -= 1
-            if self.blocks[b].ref_count == 0:
-                self._deallocate_block(b)
+    def free(self, handle):
+        """A finished sequence gives back one reference per block, its last block first
+        ([KVblog] 3.3), so a sequence's blocks join the free set tail first."""
+        s = self._seqs.pop(handle)
+        for b in reversed(s.table):
+            self._unref(b)
 
     # -- queries
-    def block_table(self, sid):
-        return list(self.seqs[sid].block_table)
+    def block_table(self, handle):
+        return list(self._seqs[handle].table)
 
-    def seq_len(self, sid):
-        return len(self.seqs[sid].token_ids)
+    def seq_len(self, handle):
+        return len(self._seqs[handle].tokens)
 
-    def num_cached_tokens(self, sid):
-        return self.seqs[sid].num_cached_tokens
+    def num_cached_tokens(self, handle):
+        return self._seqs[handle].cached
 
     def ref_count(self, block_id):
-        return self.blocks[block_id].ref_count
+        return self._refs[block_id]
 
     def num_free_blocks(self):
-        return len(self.free_block_ids)
+        return len(self._free)
+
+    def snapshot(self):
+        """The whole state, for invariant checks: reference counts, the free set in
+        order, each block's fingerprint (None if it holds nothing findable), the index,
+        and every live sequence's (token ids, block table)."""
+        return {"refs": list(self._refs), "free": list(self._free),
+                "held": [h[0] if h is not None else None for h in self._holds],
+                "index": dict(self._index),
+                "seqs": {k: (list(v.tokens), list(v.table)) for k, v in self._seqs.items()}}

@@ -1,32 +1,34 @@
 // Host-side block manager with a chain-hash prefix cache (C++, no device code).
 //
-// What is implemented follows "大模型推理引擎学习入门-2：带你理解 nano-vllm 的 KV Cache 以及
-// Paged Attention" (juejin.cn), sections 2.2, 3.3 and 3.4, and the nano-vLLM lab manual
-// ("5. 动手改造：从跑通到可测量的推理服务"), B.6:
-//  * a block's fingerprint is a chain hash: XXH64 (seed 0) over the previous full block's
-//    hash (8 bytes, little-endian; absent for the first block) followed by the block's
-//    token ids as 64-bit little-endian integers, so equal fingerprints mean equal whole
-//    prefixes; only full blocks get one;
-//  * allocate walks the prompt's blocks: a fingerprint found in the table whose block still
-//    holds the same tokens is a hit (REUSE if the block is in use: one more reference;
-//    REACTIVATE if it was freed but not yet overwritten); the first miss ends the hits for
-//    the rest of the prompt (ALLOCATE from the front of the free list); the last block of a
-//    prompt is never taken from the cache (B.6: a 512-token prompt over 256-token blocks
-//    hits at most one block), so at least one token is always computed;
-//  * freeing drops one reference per block, last block first; a block at zero goes to the
-//    back of the free list and keeps its fingerprint until it is reallocated (lazy
-//    reclamation); reallocating it drops its old fingerprint from the table;
-//  * appending a token: crossing into a new block allocates one, filling a block registers
-//    its fingerprint.  A sequence forked from another shares all its blocks (one more
-//    reference each); writing into a shared last block first gives the writer a private
-//    copy (copy-on-write, section 2.2), and the caller copies the block's K/V rows on the
-//    device with pa_copy_blocks.
+// Behaviour ("大模型推理引擎学习入门-2：带你理解 nano-vllm 的 KV Cache 以及 Paged
+// Attention" (juejin.cn), sections 2.2, 3.3 and 3.4; the nano-vLLM lab manual
+// "5. 动手改造：从跑通到可测量的推理服务", B.6):
+//  * a full block's fingerprint is a chain hash: XXH64 (seed 0) over the previous full
+//    block's fingerprint (8 bytes, little-endian; absent for the first block) followed by
+//    the block's token ids as 64-bit little-endian integers, so equal fingerprints stand
+//    for equal whole prefixes;
+//  * admitting a prompt matches its blocks against the cache from the first one on; the
+//    first block without a match ends the matching, and the prompt's last block is never
+//    matched (B.6), so at least one token is computed.  A matched block in use is shared
+//    (one more reference), a matched block that was freed but not handed out again is
+//    taken back; every other block is fresh, taken from the front of the free list and
+//    emptied (its old fingerprint leaves the index).  All full blocks of the prompt
+//    become findable under their fingerprints;
+//  * a finished sequence gives back one reference per block, last block first; a block at
+//    zero joins the back of the free list and stays findable until it is handed out
+//    again (lazy reclamation);
+//  * a generated token that starts a block gets a fresh one, a token that completes a
+//    block makes it findable.  A forked sequence shares all blocks of its parent; writing
+//    into a shared last block first moves the writer to a fresh block (copy-on-write,
+//    section 2.2) and the caller copies the block's K/V rows with pa_copy_blocks.
+//
+// Layout: per-block arrays (references, fingerprint, token ids of findable blocks) and
+// the free list as links threaded through the block ids, so that taking a freed block
+// back, wherever it sits in the list, costs O(1).
 #include <cstdint>
 #include <cstring>
-#include <deque>
 #include <new>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "pa_internal.h"
@@ -103,13 +105,6 @@ uint64_t chain_hash(const int32_t* tokens, int n, bool has_prefix, uint64_t pref
   return xxh64(buf.data(), buf.size(), 0);
 }
 
-struct Block {
-  int ref = 0;
-  bool hashed = false;  // a full block with a registered fingerprint
-  uint64_t hash = 0;
-  std::vector<int32_t> tokens;  // the block's token ids once full (for the hit check)
-};
-
 struct Seq {
   std::vector<int32_t> tokens;
   std::vector<int32_t> table;
@@ -119,52 +114,78 @@ struct Seq {
 }  // namespace
 
 struct BlockManager {
-  int32_t bs;
-  std::vector<Block> blocks;
-  std::deque<int32_t> free_ids;
-  std::unordered_set<int32_t> used;
-  std::unordered_map<uint64_t, int32_t> by_hash;
+  const int32_t bs;
+  const int32_t n;
+  std::vector<int32_t> refs;
+  std::vector<uint8_t> findable;  // the block holds a full block listed under fp
+  std::vector<uint64_t> fp;
+  std::vector<int32_t> held;      // [n][bs] token ids of findable blocks
+  std::vector<int32_t> prev, next;  // free-list links, -1 at the ends
+  int32_t head = -1, tail = -1, nfree = 0;
+  std::unordered_map<uint64_t, int32_t> index;  // fingerprint -> block
   std::unordered_map<int64_t, Seq> seqs;
-  int64_t next_id = 0;
+  int64_t next_handle = 0;
 
-  BlockManager(int32_t n, int32_t block_size) : bs(block_size), blocks(n) {
-    for (int32_t i = 0; i < n; ++i) free_ids.push_back(i);
+  BlockManager(int32_t num_blocks, int32_t block_size)
+      : bs(block_size), n(num_blocks), refs(num_blocks, 0), findable(num_blocks, 0),
+        fp(num_blocks, 0), held((size_t)num_blocks * block_size), prev(num_blocks, -1),
+        next(num_blocks, -1) {
+    for (int32_t b = 0; b < n; ++b) push_free(b);
   }
 
-  // Takes block id off the free list (front or wherever it is) into use, cleared; a
-  // fingerprint it still carried leaves the table.
-  void take(int32_t id) {
-    for (auto it = free_ids.begin(); it != free_ids.end(); ++it)
-      if (*it == id) {
-        free_ids.erase(it);
-        break;
-      }
-    Block& b = blocks[id];
-    if (b.hashed) {
-      const auto it = by_hash.find(b.hash);
-      if (it != by_hash.end() && it->second == id) by_hash.erase(it);
+  void push_free(int32_t b) {  // to the back
+    prev[b] = tail;
+    next[b] = -1;
+    if (tail >= 0) next[tail] = b;
+    else head = b;
+    tail = b;
+    ++nfree;
+  }
+  void unlink_free(int32_t b) {
+    if (prev[b] >= 0) next[prev[b]] = next[b];
+    else head = next[b];
+    if (next[b] >= 0) prev[next[b]] = prev[b];
+    else tail = prev[b];
+    prev[b] = next[b] = -1;
+    --nfree;
+  }
+  // The least recently freed block, emptied for new contents, with its first reference.
+  int32_t fresh() {
+    const int32_t b = head;
+    unlink_free(b);
+    if (findable[b]) {
+      const auto it = index.find(fp[b]);
+      if (it != index.end() && it->second == b) index.erase(it);
+      findable[b] = 0;
     }
-    b.ref = 1;
-    b.hashed = false;
-    b.tokens.clear();
-    used.insert(id);
+    refs[b] = 1;
+    return b;
   }
-  void release(int32_t id) {
-    used.erase(id);
-    free_ids.push_back(id);
+  void make_findable(int32_t b, uint64_t h, const int32_t* toks) {
+    findable[b] = 1;
+    fp[b] = h;
+    std::memcpy(&held[(size_t)b * bs], toks, sizeof(int32_t) * bs);
+    index[h] = b;
   }
-  void register_full(int32_t id, uint64_t h, const int32_t* toks) {
-    Block& b = blocks[id];
-    b.hashed = true;
-    b.hash = h;
-    b.tokens.assign(toks, toks + bs);
-    by_hash[h] = id;
+  // The block still holding exactly these tokens under this fingerprint, or -1.
+  int32_t lookup(uint64_t h, const int32_t* toks) const {
+    const auto it = index.find(h);
+    if (it == index.end()) return -1;
+    const int32_t b = it->second;
+    if (!findable[b] || fp[b] != h ||
+        std::memcmp(&held[(size_t)b * bs], toks, sizeof(int32_t) * bs) != 0)
+      return -1;
+    return b;
   }
-  // Fingerprint of logical block i of s (full), chained on block i-1's.
-  uint64_t hash_of(const Seq& s, int i, uint64_t prev) const {
-    return chain_hash(s.tokens.data() + (size_t)i * bs, bs, i > 0, prev);
+  void unref(int32_t b) {
+    if (--refs[b] == 0) push_free(b);  // keeps what it holds
   }
-  int32_t free_count() const { return (int32_t)free_ids.size(); }
+  // Chain fingerprints of the first `count` full blocks of a token list.
+  void fingerprints(const int32_t* toks, int count, std::vector<uint64_t>& out) const {
+    out.resize(count);
+    for (int i = 0; i < count; ++i)
+      out[i] = chain_hash(toks + (size_t)i * bs, bs, i > 0, i > 0 ? out[i - 1] : 0);
+  }
 };
 
 }  // namespace pa
@@ -187,7 +208,12 @@ extern "C" pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size
     fail(PA_ERR_SHAPE, "pa_bm_create: num_blocks %d, block_size %d", num_blocks, block_size);
     return nullptr;
   }
-  return new (std::nothrow) pa_block_manager(num_blocks, block_size);
+  try {
+    return new pa_block_manager(num_blocks, block_size);
+  } catch (const std::bad_alloc&) {
+    fail(PA_ERR_CAPACITY, "pa_bm_create: out of host memory for %d blocks", num_blocks);
+    return nullptr;
+  }
 }
 
 extern "C" void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
@@ -198,44 +224,38 @@ extern "C" int64_t pa_bm_allocate(pa_block_manager* bm, const int32_t* token_ids
   if (!bm || (!token_ids && num_tokens > 0)) return -fail(PA_ERR_NULL, "pa_bm_allocate: null");
   if (num_tokens <= 0) return -fail(PA_ERR_SHAPE, "pa_bm_allocate: %d tokens", num_tokens);
   BlockManager& m = bm->m;
-  const int nb = (num_tokens + m.bs - 1) / m.bs;
-  if (nb > m.free_count()) {
-    // The walk below may reuse blocks, but admission is decided on the worst case.
-    return -fail(PA_ERR_CAPACITY, "pa_bm_allocate: %d blocks needed, %d free", nb, m.free_count());
+  const int need = (num_tokens + m.bs - 1) / m.bs;
+  if (need > m.nfree)  // decided on the worst case: no block found in the cache
+    return -fail(PA_ERR_CAPACITY, "pa_bm_allocate: %d blocks needed, %d free", need, m.nfree);
+  const int full = num_tokens / m.bs;
+  std::vector<uint64_t> fps;
+  m.fingerprints(token_ids, full, fps);
+  // The cached run at the front of the prompt (never its last block).
+  std::vector<int32_t> table;
+  table.reserve(need);
+  for (int i = 0; i < full && i < need - 1; ++i) {
+    const int32_t b = m.lookup(fps[i], token_ids + (size_t)i * m.bs);
+    if (b < 0) break;
+    table.push_back(b);
   }
+  const int matched = (int)table.size();
+  for (const int32_t b : table) {
+    if (m.refs[b] > 0) {
+      ++m.refs[b];  // shared with a live sequence
+    } else {
+      m.unlink_free(b);  // freed but intact: back in use
+      m.refs[b] = 1;
+    }
+  }
+  while ((int)table.size() < need) table.push_back(m.fresh());
+  for (int i = 0; i < full; ++i) m.make_findable(table[i], fps[i], token_ids + (size_t)i * m.bs);
   Seq s;
   s.tokens.assign(token_ids, token_ids + num_tokens);
-  bool miss = false;
-  uint64_t h = 0;
-  for (int i = 0; i < nb; ++i) {
-    const bool full = (i + 1) * m.bs <= num_tokens;
-    if (full) h = m.hash_of(s, i, h);
-    int32_t id = -1;
-    if (full && i < nb - 1 && !miss) {  // the prompt's last block is always computed
-      const auto it = m.by_hash.find(h);
-      if (it != m.by_hash.end()) {
-        const Block& b = m.blocks[it->second];
-        if (b.hashed && b.hash == h &&
-            std::memcmp(b.tokens.data(), s.tokens.data() + (size_t)i * m.bs,
-                        sizeof(int32_t) * m.bs) == 0)
-          id = it->second;
-      }
-    }
-    if (id < 0) {
-      miss = true;
-      id = m.free_ids.front();
-      m.take(id);  // ALLOCATE
-    } else {
-      s.cached += m.bs;
-      if (m.used.count(id)) ++m.blocks[id].ref;  // REUSE
-      else m.take(id);                             // REACTIVATE
-    }
-    if (full) m.register_full(id, h, s.tokens.data() + (size_t)i * m.bs);
-    s.table.push_back(id);
-  }
-  const int64_t sid = m.next_id++;
-  m.seqs.emplace(sid, std::move(s));
-  return sid;
+  s.table = std::move(table);
+  s.cached = matched * m.bs;
+  const int64_t handle = m.next_handle++;
+  m.seqs.emplace(handle, std::move(s));
+  return handle;
 }
 
 extern "C" int pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t token_id,
@@ -248,27 +268,26 @@ extern "C" int pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t token_id,
   Seq& s = it->second;
   if (cow_src) *cow_src = -1;
   if (cow_dst) *cow_dst = -1;
-  const int len = (int)s.tokens.size() + 1;  // after the append
-  if (len % m.bs == 1) {  // the token opens a new block
-    if (m.free_count() == 0) return fail(PA_ERR_CAPACITY, "pa_bm_append: no free block");
-    const int32_t id = m.free_ids.front();
-    m.take(id);
-    s.table.push_back(id);
-  } else if (m.blocks[s.table.back()].ref > 1) {  // shared partial block: copy on write
-    if (m.free_count() == 0) return fail(PA_ERR_CAPACITY, "pa_bm_append: no free block");
-    const int32_t src = s.table.back();
-    const int32_t id = m.free_ids.front();
-    m.take(id);
-    --m.blocks[src].ref;
-    s.table.back() = id;
-    if (cow_src) *cow_src = src;
-    if (cow_dst) *cow_dst = id;
+  const int len = (int)s.tokens.size() + 1;  // with the new token
+  const bool starts = len % m.bs == 1;  // block_size >= 2
+  if (starts || m.refs[s.table.back()] > 1) {
+    if (m.nfree == 0) return fail(PA_ERR_CAPACITY, "pa_bm_append: no free block");
+    if (starts) {
+      s.table.push_back(m.fresh());
+    } else {  // the last block is shared: move to a private copy
+      const int32_t src = s.table.back();
+      s.table.back() = m.fresh();
+      --m.refs[src];  // others still hold it
+      if (cow_src) *cow_src = src;
+      if (cow_dst) *cow_dst = s.table.back();
+    }
   }
   s.tokens.push_back(token_id);
-  if (len % m.bs == 0) {  // the token fills its block: register the fingerprint
+  if (len % m.bs == 0) {  // the token completes its block
     const int i = len / m.bs - 1;
-    const uint64_t prev = i > 0 ? m.blocks[s.table[i - 1]].hash : 0;
-    m.register_full(s.table[i], m.hash_of(s, i, prev), s.tokens.data() + (size_t)i * m.bs);
+    std::vector<uint64_t> fps;
+    m.fingerprints(s.tokens.data(), i + 1, fps);
+    m.make_findable(s.table[i], fps[i], s.tokens.data() + (size_t)i * m.bs);
   }
   return PA_OK;
 }
@@ -279,11 +298,11 @@ extern "C" int64_t pa_bm_fork(pa_block_manager* bm, int64_t seq) {
   BlockManager& m = bm->m;
   auto it = m.seqs.find(seq);
   if (it == m.seqs.end()) return -fail(PA_ERR_SHAPE, "pa_bm_fork: no sequence %lld", (long long)seq);
+  for (const int32_t b : it->second.table) ++m.refs[b];
   Seq child = it->second;
-  for (int32_t id : child.table) ++m.blocks[id].ref;
-  const int64_t sid = m.next_id++;
-  m.seqs.emplace(sid, std::move(child));
-  return sid;
+  const int64_t handle = m.next_handle++;
+  m.seqs.emplace(handle, std::move(child));
+  return handle;
 }
 
 extern "C" int pa_bm_free(pa_block_manager* bm, int64_t seq) {
@@ -293,8 +312,7 @@ extern "C" int pa_bm_free(pa_block_manager* bm, int64_t seq) {
   auto it = m.seqs.find(seq);
   if (it == m.seqs.end()) return fail(PA_ERR_SHAPE, "pa_bm_free: no sequence %lld", (long long)seq);
   const std::vector<int32_t>& t = it->second.table;
-  for (auto r = t.rbegin(); r != t.rend(); ++r)
-    if (--m.blocks[*r].ref == 0) m.release(*r);
+  for (auto r = t.rbegin(); r != t.rend(); ++r) m.unref(*r);  // last block first
   m.seqs.erase(it);
   return PA_OK;
 }
@@ -326,10 +344,10 @@ extern "C" int32_t pa_bm_num_cached_tokens(const pa_block_manager* bm, int64_t s
 
 extern "C" int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block_id) {
   if (!bm) return -PA_ERR_NULL;
-  if (block_id < 0 || block_id >= (int32_t)bm->m.blocks.size()) return -PA_ERR_SHAPE;
-  return bm->m.blocks[block_id].ref;
+  if (block_id < 0 || block_id >= bm->m.n) return -PA_ERR_SHAPE;
+  return bm->m.refs[block_id];
 }
 
 extern "C" int32_t pa_bm_num_free_blocks(const pa_block_manager* bm) {
-  return bm ? bm->m.free_count() : -PA_ERR_NULL;
+  return bm ? bm->m.nfree : -PA_ERR_NULL;
 }

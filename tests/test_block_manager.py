@@ -28,24 +28,22 @@ def lib():
     return pk.lib()
 
 
-def check_invariants(m: obm.BlockManager):
-    """Reference counts equal table memberships; free and used blocks split the pool;
-    every table has ceil(len / block_size) entries; the hash table names registered
-    blocks only."""
-    refs = [0] * len(m.blocks)
-    for s in m.seqs.values():
-        assert len(s.block_table) == -(-len(s.token_ids) // m.block_size)
-        for b in s.block_table:
+def check_invariants(m):
+    """Reference counts equal table memberships; the free set holds exactly the blocks
+    with no reference, each once; every table has ceil(len / block_size) entries; the
+    index names blocks that hold the fingerprint it maps."""
+    st = m.snapshot()
+    refs = [0] * m.num_blocks
+    for tokens, table in st["seqs"].values():
+        assert len(table) == -(-len(tokens) // m.block_size)
+        for b in table:
             refs[b] += 1
-    assert refs == [b.ref_count for b in m.blocks]
-    free = list(m.free_block_ids)
+    assert refs == st["refs"]
+    free = st["free"]
     assert len(free) == len(set(free))
-    assert set(free).isdisjoint(m.used_block_ids)
-    assert set(free) | m.used_block_ids == set(range(len(m.blocks)))
-    assert all(m.blocks[b].ref_count == 0 for b in free)
-    assert all(m.blocks[b].ref_count > 0 for b in m.used_block_ids)
-    for h, b in m.hash_to_block_id.items():
-        assert m.blocks[b].hash == h
+    assert set(free) == {b for b in range(m.num_blocks) if st["refs"][b] == 0}
+    for fp, b in st["index"].items():
+        assert st["held"][b] == fp
 
 
 # ---------------------------------------------------------------- oracle pins
@@ -117,7 +115,7 @@ def pin_kvblog_allocate_and_free_log(mod):
     m.free(ids[1])
     assert m.num_free_blocks() == ex["free_second"]["free_blocks"]
     assert m.ref_count(0) == ex["free_second"]["ref_count_block0"]
-    assert list(m.free_block_ids)[-3:] == ex["free_second"]["free_list_tail"]
+    assert m.snapshot()["free"][-3:] == ex["free_second"]["free_list_tail"]
     check_invariants(m)
 
 
@@ -130,7 +128,8 @@ def pin_kvblog_may_append_table(mod):
     for n in range(256, 514):
         m.append(s, 1000 + n)
         if n in rows:
-            registered = sum(1 for b in m.block_table(s) if m.blocks[b].hash is not None)
+            held = m.snapshot()["held"]
+            registered = sum(1 for b in m.block_table(s) if held[b] is not None)
             assert len(m.block_table(s)) == rows[n]["blocks"], n
             assert registered == rows[n]["registered"], n
     check_invariants(m)
@@ -285,7 +284,7 @@ def random_operations(mod, seed, steps=400, each=None):
         check_invariants(m)
     for s in live:
         m.free(s)
-    assert m.num_free_blocks() == len(m.blocks)
+    assert m.num_free_blocks() == m.num_blocks
     check_invariants(m)
 
 
@@ -320,20 +319,27 @@ def _fresh_oracle(old=None, new=None):
 
 MUTANTS = [
     ("hash ignores the prefix", 'h.update(int(prefix).to_bytes(8, "little"))', "pass"),
-    ("REUSE forgets the reference", "                    block.ref_count += 1\n", "                    pass\n"),
-    ("a miss does not end the hits", "            if cache_miss:  # ALLOCATE", "            if block_id < 0:  # ALLOCATE"),
-    ("the last block is looked up", "if full and i < nb - 1:", "if full:"),
-    ("no token comparison", "self.blocks[cand].token_ids == tokens", "True"),
-    ("cached tokens not counted", "seq.num_cached_tokens += self.block_size", "pass"),
-    ("REACTIVATE taken as REUSE", "if block_id in self.used_block_ids:  # REUSE", "if True:  # REUSE"),
-    ("free walks first block first", "for b in reversed(seq.block_table):", "for b in seq.block_table:"),
-    ("freed block to the front", "self.free_block_ids.append(block_id)", "self.free_block_ids.appendleft(block_id)"),
-    ("new block on % == 0", "if n % self.block_size == 1:  # the token opens", "if n % self.block_size == 0:  # the token opens"),
-    ("register on % == 1", "if n % self.block_size == 0:  # the token fills", "if n % self.block_size == 1:  # the token fills"),
-    ("no copy-on-write", "elif self.blocks[seq.block_table[-1]].ref_count > 1:", "elif False:"),
-    ("fork adds no references", "            self.blocks[b].ref_count += 1\n", "            pass\n"),
-    ("stale mapping kept", "            del self.hash_to_block_id[block.hash]", "            pass"),
-    ("capacity off by one", "return len(self.free_block_ids) >= self._num_blocks(n)", "return len(self.free_block_ids) >= self._num_blocks(n) - 1"),
+    ("sharing forgets the reference", "self._refs[b] += 1  # shared with a live sequence",
+     "pass  # shared with a live sequence"),
+    ("a miss does not end the matching", "            if b is None:\n                break",
+     "            if b is None:\n                continue"),
+    ("the last block is matched", "for i in range(min(len(fps), need - 1)):", "for i in range(len(fps)):"),
+    ("no token comparison", "self._holds[b] == (fp, tokens)", "self._holds[b] is not None"),
+    ("cached tokens not counted", "len(matched) * self.block_size)", "0)"),
+    ("a freed block shared instead of taken back", "            if self._refs[b] > 0:\n",
+     "            if True:\n"),
+    ("free walks first block first", "for b in reversed(s.table):", "for b in s.table:"),
+    ("freed block to the front", "self._free[b] = None  # joins the back",
+     "self._free[b] = None; self._free.move_to_end(b, last=False)  # joins the back"),
+    ("new block on % == 0", "if n % self.block_size == 1:  # the token starts",
+     "if n % self.block_size == 0:  # the token starts"),
+    ("findable on % == 1", "if n % self.block_size == 0:  # the token completes",
+     "if n % self.block_size == 1:  # the token completes"),
+    ("no copy-on-write", "elif self._refs[s.table[-1]] > 1:", "elif False:"),
+    ("fork adds no references", "        for b in s.table:\n            self._refs[b] += 1\n",
+     "        for b in s.table:\n            pass\n"),
+    ("stale index entry kept", "            del self._index[held[0]]", "            pass"),
+    ("capacity off by one", "if len(self._free) < need:", "if len(self._free) < need - 1:"),
 ]
 
 
@@ -372,7 +378,7 @@ class Both:
     def same(self):
         o, n = self.o, self.n
         assert o.num_free_blocks() == n.num_free_blocks()
-        for b in range(len(o.blocks)):
+        for b in range(o.num_blocks):
             assert o.ref_count(b) == n.ref_count(b), b
         for so, sn in self.ids.items():
             assert o.block_table(so) == n.block_table(sn)
@@ -469,7 +475,7 @@ def test_native_random_operations(lib, seed):
     for s in live:
         bm.free(s)
     bm.same()
-    assert bm.o.num_free_blocks() == len(bm.o.blocks)
+    assert bm.o.num_free_blocks() == bm.o.num_blocks
 
 
 def test_native_errors(lib):
