@@ -250,7 +250,8 @@ def _graph_us(fn, reps, rounds=5):
 def time_graphs(w, dw, args):
     """Decode steps (slot addressing + scatter + decode + merge) for the first n sequences
     of the decode batch: launched eagerly from Python against replayed from the HIP graph
-    of their batch bucket (inputs copied into the graph's fixed buffers each step)."""
+    of their batch bucket, with the inputs staged into the graph's fixed buffers each step
+    (one pa_copy_many launch) and with them already in place (bare replay)."""
     import torch
 
     import paged_kv_cache_67_amd as pk
@@ -300,7 +301,7 @@ def time_graphs(w, dw, args):
                        "us_graph_replay": round(timing["replay"], 2), "outputs_identical": same}
         log(f"graphs: batch {n}: eager {timing['eager']:.1f} us/step; graph (bucket "
             f"{runner.bucket(n)}) {timing['replay']:.1f} us/step with the inputs in its buffers, "
-            f"{timing['graph']:.1f} with six torch copies in; identical {same}")
+            f"{timing['graph']:.1f} with the inputs staged in by one pa_copy_many; identical {same}")
     return {"workload": w.name, "steps": steps, "by_batch": res,
             "timing": "events around back-to-back steps launched from Python"}
 

@@ -368,6 +368,34 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
                    int32_t head_dim, pa_dtype dtype, void* stream);
 
 /*
+ * pa_copy_many -- up to PA_COPY_MANY_MAX device copies and zero fills in one
+ * launch.
+ *
+ * [Lab] B.4: a decode step replayed from a captured graph first copies its
+ * inputs (q, new K/V rows, block table, lengths) into the fixed buffers the
+ * graph was captured over, and marks the padding rows of its batch bucket.
+ * This does all of those copies in one launch instead of one per tensor.
+ *
+ *   descs   HOST array of count descriptors {src, dst, bytes}: bytes >= 0 and a
+ *           multiple of 4, src and dst DEVICE pointers, 4-byte aligned (16-byte
+ *           aligned pointers and sizes take the 16-byte path); src NULL fills
+ *           dst with zeros.  Destinations must not overlap each other or any
+ *           source.
+ *   count   0 .. PA_COPY_MANY_MAX
+ *
+ * The descriptors are passed by value to the kernel: the host array may be
+ * reused as soon as the call returns.  Errors: PA_ERR_SHAPE, PA_ERR_NULL,
+ * PA_ERR_ALIGN, PA_ERR_HIP.
+ */
+#define PA_COPY_MANY_MAX 8
+typedef struct pa_copy_desc {
+  const void* src;
+  void* dst;
+  int64_t bytes;
+} pa_copy_desc;
+int pa_copy_many(const pa_copy_desc* descs, int32_t count, void* stream);
+
+/*
  * pa_read_ceiling -- measurement helper: the read bandwidth the decode pass
  * can reach.  Not part of the attention path.
  *

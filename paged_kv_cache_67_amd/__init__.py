@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     pa_check_prefill_inputs,
     pa_check_store_inputs,
     pa_copy_blocks,
+    pa_copy_many,
     pa_read_ceiling,
     pa_decode,
     pa_decode_merge,

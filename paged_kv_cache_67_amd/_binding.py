@@ -24,6 +24,14 @@ STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTE
 _i32, _i64, _f32, _vp, _sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 _u64, _pi32 = C.c_uint64, C.POINTER(C.c_int32)
 
+PA_COPY_MANY_MAX = 8
+
+
+class CopyDesc(C.Structure):
+    """pa_copy_desc: {src (NULL = zero fill), dst, bytes}."""
+    _fields_ = [("src", _vp), ("dst", _vp), ("bytes", _i64)]
+
+
 # name -> (restype, argtypes); mirrors include/pa.h
 SIGNATURES = {
     "pa_version": (C.c_int, []),
@@ -47,6 +55,7 @@ SIGNATURES = {
                                      _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _vp, _sz,
                                      _vp]),
     "pa_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pa_copy_many": (C.c_int, [C.POINTER(CopyDesc), _i32, _vp]),
     "pa_read_ceiling": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, C.c_int, _i32,
                                   _vp, _vp]),
     "pa_set_debug_checks": (C.c_int, [C.c_int]),
@@ -313,6 +322,32 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
     _check("pa_copy_blocks", lib().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0], NB, BS, HKV, D,
         _dtype(k_cache), _stream(stream)))
+
+
+def copy_descs(n=PA_COPY_MANY_MAX):
+    """A reusable host array of n pa_copy_desc."""
+    return (CopyDesc * n)()
+
+
+def pa_copy_many(pairs, stream=None, descs=None):
+    """Copies src -> dst for each (src, dst) in pairs (src None: zero dst) in one launch.
+    Tensors are contiguous device tensors; src and dst of a pair have the same byte size.
+    descs: an optional array from copy_descs() to fill instead of a new one."""
+    if len(pairs) > PA_COPY_MANY_MAX:
+        raise ValueError(f"at most {PA_COPY_MANY_MAX} copies per call")
+    if descs is None:
+        descs = copy_descs(len(pairs))
+    for k, (src, dst) in enumerate(pairs):
+        assert dst.is_contiguous() and dst.is_cuda
+        nbytes = dst.numel() * dst.element_size()
+        if src is not None:
+            assert src.is_contiguous() and src.is_cuda
+            assert src.numel() * src.element_size() == nbytes, "src and dst sizes differ"
+        d = descs[k]
+        d.src = src.data_ptr() if src is not None else None
+        d.dst = dst.data_ptr()
+        d.bytes = nbytes
+    _check("pa_copy_many", lib().pa_copy_many(descs, len(pairs), _stream(stream)))
 
 
 def pa_read_ceiling(k_cache, v_cache, block_ids, num_workgroups, sink, stream=None):

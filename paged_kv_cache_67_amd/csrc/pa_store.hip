@@ -79,9 +79,68 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* kc, char* vc,
   }
 }
 
+// Several device copies and zero fills in one launch: the staging of a step's inputs into
+// the fixed buffers a captured graph replays over ("5. 动手改造：从跑通到可测量的推理服务",
+// B.4: each step's inputs are copied into the captured buffers, then the graph is replayed).
+// The descriptors travel by value in the kernel arguments; each is walked in 16-byte
+// chunks when its pointers and size allow, else in 4-byte words.
+struct CopyList {
+  pa_copy_desc d[PA_COPY_MANY_MAX];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void copy_many_kernel(CopyList list) {
+  const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int k = 0; k < list.n; ++k) {
+    const pa_copy_desc d = list.d[k];
+    const bool wide = ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst) |
+                        (uint64_t)d.bytes) & 15) == 0;
+    if (wide) {
+      const int64_t n = d.bytes / 16;
+      const uint4* src = reinterpret_cast<const uint4*>(d.src);
+      uint4* dst = reinterpret_cast<uint4*>(d.dst);
+      for (int64_t i = first; i < n; i += step) dst[i] = src ? src[i] : make_uint4(0, 0, 0, 0);
+    } else {
+      const int64_t n = d.bytes / 4;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(d.src);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(d.dst);
+      for (int64_t i = first; i < n; i += step) dst[i] = src ? src[i] : 0u;
+    }
+  }
+}
+
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" int pa_copy_many(const pa_copy_desc* descs, int32_t count, void* stream) {
+  clear_error();
+  if (count < 0 || count > PA_COPY_MANY_MAX)
+    return fail(PA_ERR_SHAPE, "pa_copy_many: %d descriptors (0 to %d)", count, PA_COPY_MANY_MAX);
+  if (count == 0) return PA_OK;
+  if (!descs) return fail(PA_ERR_NULL, "pa_copy_many: null descriptor list");
+  CopyList list{};
+  int64_t most = 0;
+  for (int k = 0; k < count; ++k) {
+    const pa_copy_desc& d = descs[k];
+    if (d.bytes < 0 || d.bytes % 4)
+      return fail(PA_ERR_SHAPE, "pa_copy_many: descriptor %d has %lld bytes (a multiple of 4)", k,
+                  (long long)d.bytes);
+    if (d.bytes > 0 && !d.dst) return fail(PA_ERR_NULL, "pa_copy_many: descriptor %d: null dst", k);
+    if ((reinterpret_cast<uintptr_t>(d.src) | reinterpret_cast<uintptr_t>(d.dst)) & 3)
+      return fail(PA_ERR_ALIGN, "pa_copy_many: descriptor %d: pointers must be 4-byte aligned", k);
+    list.d[k] = d;
+    most = d.bytes > most ? d.bytes : most;
+  }
+  list.n = count;
+  if (most == 0) return PA_OK;
+  const int64_t chunks = (most + 15) / 16;
+  const int64_t blocks = (chunks + 255) / 256;
+  const int grid = int(blocks < 1024 ? blocks : 1024);
+  hipLaunchKernelGGL(copy_many_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, list);
+  return check_launch("pa_copy_many");
+}
 
 extern "C" int pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_table,
                                int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,

@@ -15,12 +15,18 @@ launches are the eager ones.
     runner = GraphedDecode(k_cache, v_cache, num_q_heads=16, max_blocks_per_seq=16,
                            max_context_len=4096, scale=1 / 128 ** 0.5, max_batch=256)
     out = runner.step(q, k_new, v_new, block_table, context_lens)
+
+``step`` stages the live rows into the graph's buffers with one pa_copy_many
+launch (all five inputs and the padding rows' zero lengths) and replays.  A
+caller that can produce its inputs in place writes them into the views
+``inputs(n)`` returns and calls ``replay(n)``, which copies nothing.
 """
 
 from __future__ import annotations
 
 import bisect
 
+import numpy as np
 import torch
 
 from . import _binding as pa
@@ -66,6 +72,25 @@ class GraphedDecode:
         nbytes = pa.pa_decode_workspace_size(bmax, num_q_heads, HKV, D, self.max_context_len, 0)
         self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=dev)
         self.graphs = {}
+        # Staging: one descriptor per input (q, k_new, v_new, block_table, context_lens), then
+        # the zero lengths of the padding rows; destinations are the fixed buffers.
+        # The descriptors are also viewed as an int64 [6][3] array (src, dst, bytes) so that a
+        # step fills them with two vector assignments.
+        self._descs = pa.copy_descs(6)
+        self._desc_rows = np.frombuffer(self._descs, dtype=np.int64).reshape(6, 3)
+        bufs = (self.q, self.k_new, self.v_new, self.block_table, self.context_lens)
+        self._desc_rows[:5, 1] = [t.data_ptr() for t in bufs]
+        self._row_bytes = np.array([t[0].numel() * t.element_size() for t in bufs], dtype=np.int64)
+        self._copy_many = pa.lib().pa_copy_many
+        self._bucket_of = [self.bucket(n) for n in range(bmax + 1)]
+        self._out_rows = [self.out[:n] for n in range(bmax + 1)]
+        self._width = max_blocks_per_seq
+        # The staging goes to the stream the replay will run on (torch's current stream);
+        # torch's raw-stream query is the cheap way to name it.
+        self._device = dev.index if dev.index is not None else torch.cuda.current_device()
+        self._raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream",
+                                   lambda d: torch.cuda.current_stream(d).cuda_stream)
+        self._hi = 0  # rows [self._hi, bmax) of context_lens are known to be 0
 
     def bucket(self, batch):
         """The smallest bucket that holds `batch` rows, or None if none does."""
@@ -107,13 +132,58 @@ class GraphedDecode:
                      max_context_len=self.max_context_len, partition_size=0, workspace=ws)
         return out
 
-    def step(self, q, k_new, v_new, block_table, context_lens):
-        """One decode step for the live rows; returns a view of the output rows (a new
-        tensor when the batch is larger than every bucket and runs eagerly)."""
-        n = q.shape[0]
+    def inputs(self, n):
+        """Views of the fixed buffers for a batch of n rows, to be written in place:
+        (q, k_new, v_new, block_table, context_lens); then call replay(n)."""
+        return (self.q[:n], self.k_new[:n], self.v_new[:n], self.block_table[:n],
+                self.context_lens[:n])
+
+    def replay(self, n):
+        """Replays n's bucket over the rows already in the buffers (see inputs); the rows
+        between n and the bucket get length 0 (one zero fill, only when fewer rows are
+        live than at the bucket's last replay).  Returns a view of the output rows."""
         b = self.bucket(n)
         if b is None:
+            raise ValueError(f"batch {n} exceeds the largest bucket {self.buckets[-1]}")
+        end = min(self._hi, b)
+        if end > n:
+            pa.pa_copy_many([(None, self.context_lens[n:end])])
+        self._padded(n, b)
+        self.capture(b).replay()
+        return self.out[:n]
+
+    def _padded(self, n, b):
+        """Rows [n, b) were just zeroed and rows [0, n) hold live lengths: rows past the
+        bucket may still hold lengths of an earlier, larger batch."""
+        self._hi = self._hi if self._hi > b else n
+
+    def step(self, q, k_new, v_new, block_table, context_lens):
+        """One decode step for the live rows; returns a view of the output rows (a new
+        tensor when the batch is larger than every bucket and runs eagerly).  The inputs
+        are staged into the graph's buffers by one pa_copy_many launch."""
+        n = q.shape[0]
+        b = self._bucket_of[n] if n < len(self._bucket_of) else None
+        if b is None:
             return self.eager(q, k_new, v_new, block_table, context_lens)
+        srcs = (q, k_new, v_new, block_table, context_lens)
+        if block_table.shape[1] != self._width or not all(t.is_contiguous() for t in srcs):
+            return self._step_torch(q, k_new, v_new, block_table, context_lens, n, b)
+        rows = self._desc_rows
+        rows[:5, 0] = [t.data_ptr() for t in srcs]
+        rows[:5, 2] = self._row_bytes * n
+        # padding rows: no keys, no cache write
+        rows[5] = (0, rows[4, 1] + 4 * n, 4 * (b - n))
+        st = self._copy_many(self._descs, 6, self._raw_stream(self._device))
+        if st:
+            pa._check("pa_copy_many", st)
+        self._padded(n, b)
+        g = self.graphs.get(b)
+        (g if g is not None else self.capture(b)).replay()
+        return self._out_rows[n]
+
+    def _step_torch(self, q, k_new, v_new, block_table, context_lens, n, b):
+        """Staging by separate torch copies (a block table narrower than the buffer's, or
+        inputs that are not contiguous)."""
         self.q[:n].copy_(q)
         self.k_new[:n].copy_(k_new)
         self.v_new[:n].copy_(v_new)
@@ -123,6 +193,6 @@ class GraphedDecode:
             self.block_table[:n, w:].fill_(-1)
         self.context_lens[:n].copy_(context_lens)
         self.context_lens[n:b].zero_()  # padding rows: no keys, no cache write
-        g = self.capture(b)
-        g.replay()
+        self._padded(n, b)
+        self.capture(b).replay()
         return self.out[:n]

@@ -181,6 +181,23 @@ def test_mixed_sequence_limit(L, head_dim):
     assert f"at most {n}" in pk.pa_last_error()
 
 
+def test_copy_many_validation(L):
+    d = B.copy_descs(9)
+    assert L.pa_copy_many(d, 0, None) == 0
+    assert L.pa_copy_many(d, 9, None) == 2          # more than PA_COPY_MANY_MAX
+    assert L.pa_copy_many(None, 1, None) == 1
+    d[0].src, d[0].dst, d[0].bytes = 0x10000, 0x20000, 6   # not a multiple of 4
+    assert L.pa_copy_many(d, 1, None) == 2
+    d[0].bytes = -4
+    assert L.pa_copy_many(d, 1, None) == 2
+    d[0].dst, d[0].bytes = None, 16
+    assert L.pa_copy_many(d, 1, None) == 1
+    d[0].src, d[0].dst = 0x10002, 0x20000                   # 2-byte aligned
+    assert L.pa_copy_many(d, 1, None) == 4
+    d[0].src, d[0].dst, d[0].bytes = None, None, 0          # empty: nothing to launch
+    assert L.pa_copy_many(d, 1, None) == 0
+
+
 def test_read_ceiling_validation(L):
     a = ctypes.c_void_p(0x10000)
     # (k, v, ids, num_ids, num_blocks, block_size, kv_heads, head_dim, dtype, workgroups, sink, stream)

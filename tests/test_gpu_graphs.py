@@ -94,3 +94,77 @@ def test_batch_past_every_bucket_runs_eagerly():
     torch.cuda.synchronize()
     assert not runner.graphs
     assert_close(out_f64(out, "bf16"), ref.decode(idx), "bf16", "eager fallback")
+
+
+def test_direct_writes_and_stale_rows_across_buckets():
+    """The in-place route (inputs + replay): the caller writes each batch straight into the
+    runner's buffers.  Batches shrink across buckets so that rows past a small bucket still
+    hold lengths of an earlier large batch; the padding rows of every replay must be zero
+    (else their stale lengths would store rows into the pool).  Outputs match the oracle,
+    the pools match it bit for bit."""
+    w, dw = _setup(B=40, seed=34)
+    ref = OracleRun(w)
+    runner = GraphedDecode(dw.k_cache, dw.v_cache, w.num_q_heads, w.block_table.shape[1],
+                           int(w.seq_lens_k.max()), w.scale, buckets=(4, 16, 32, 40))
+    plan = [np.arange(0, 30), np.arange(30, 40)]  # 30 rows (bucket 32), then 10 (bucket 16)
+    for idx in plan:
+        n = len(idx)
+        announce(f"in-place graph step, batch {n} -> bucket {runner.bucket(n)}")
+        for dst, src in zip(runner.inputs(n), _rows(dw, idx)):
+            dst.copy_(src)
+        out = runner.replay(n)
+        torch.cuda.synchronize()
+        assert_close(out_f64(out, "bf16"), ref.decode(idx), "bf16", f"in place, batch {n}")
+        assert torch.count_nonzero(runner.context_lens[n:runner.bucket(n)]).item() == 0
+    # a 3-row step through the staged route after the larger ones: row 3 of bucket 4 is
+    # padding, and rows 10..29 past bucket 16 still hold the 30-row batch's lengths
+    idx = np.array([1, 2, 3])
+    q, kn, vn, bt, ctx = _rows(dw, idx)
+    announce("staged graph step, batch 3 after a 30-row batch")
+    out = runner.step(q, kn, vn, bt, ctx)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(runner.context_lens[3:4]).item() == 0
+    # the 3 rows were stored twice (same bits); every sequence's row is in the pool
+    assert_close(out_f64(out, "bf16"), ref.decode(idx), "bf16", "batch 3")
+    assert bits_equal(harness.from_device(dw.k_cache), ref.k_pool)
+    assert bits_equal(harness.from_device(dw.v_cache), ref.v_pool)
+
+
+def test_narrow_block_table_takes_the_torch_staging():
+    w, dw = _setup(B=12, seed=35)
+    ref = OracleRun(w)
+    wide = w.block_table.shape[1] + 3
+    runner = GraphedDecode(dw.k_cache, dw.v_cache, w.num_q_heads, wide,
+                           int(w.seq_lens_k.max()), w.scale, buckets=(16,))
+    idx = np.arange(12)
+    announce("graph step with a block table narrower than the runner's")
+    out = runner.step(*_rows(dw, idx))
+    torch.cuda.synchronize()
+    assert_close(out_f64(out, "bf16"), ref.decode(idx), "bf16", "narrow table")
+    assert (runner.block_table[:12, w.block_table.shape[1]:] == -1).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_copy_many_copies_and_zero_fills(seed):
+    """pa_copy_many: copies bit for bit and zero fills, sizes on and off the 16-byte path
+    (4-byte multiples, views starting 4 bytes into a buffer), one launch."""
+    import paged_kv_cache_67_amd as pk
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    sizes = [4, 12, 16, 260, 4096, 65540, 1 << 20]
+    pairs, keep = [], []
+    for k, nb in enumerate(sizes):
+        src = torch.randint(-2**31, 2**31 - 1, (nb // 4 + 1,), dtype=torch.int32, generator=g).cuda()
+        dst = torch.full((nb // 4 + 2,), 7, dtype=torch.int32, device="cuda")
+        off = k % 2  # every other pair starts one word in: 4-byte aligned, not 16
+        s_view, d_view = src[off:off + nb // 4], dst[off:off + nb // 4]
+        pairs.append((s_view, d_view))
+        keep.append((src, dst, off, nb // 4))
+    zero = torch.full((1000,), 9, dtype=torch.int32, device="cuda")
+    pairs.append((None, zero[4:996]))
+    announce(f"pa_copy_many, {len(pairs)} descriptors")
+    pk.pa_copy_many(pairs)
+    torch.cuda.synchronize()
+    for src, dst, off, n in keep:
+        assert torch.equal(dst[off:off + n], src[off:off + n])
+        assert (dst[:off] == 7).all() and (dst[off + n:] == 7).all()  # nothing past the view
+    assert (zero[4:996] == 0).all() and (zero[:4] == 9).all() and (zero[996:] == 9).all()
