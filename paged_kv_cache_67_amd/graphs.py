@@ -74,15 +74,24 @@ class GraphedDecode:
         self.graphs = {}
         # Staging: one descriptor per input (q, k_new, v_new, block_table, context_lens), then
         # the zero lengths of the padding rows; destinations are the fixed buffers.
-        # The descriptors are also viewed as an int64 [6][3] array (src, dst, bytes) so that a
-        # step fills them with two vector assignments.
-        self._descs = pa.copy_descs(6)
-        self._desc_rows = np.frombuffer(self._descs, dtype=np.int64).reshape(6, 3)
+        # One descriptor list per batch size, its destinations and sizes filled in advance
+        # (the padding rows' lengths are the sixth, a zero fill); a step only writes the five
+        # source pointers, through an int64 [6][3] view (src, dst, bytes) of the list.
         bufs = (self.q, self.k_new, self.v_new, self.block_table, self.context_lens)
-        self._desc_rows[:5, 1] = [t.data_ptr() for t in bufs]
-        self._row_bytes = np.array([t[0].numel() * t.element_size() for t in bufs], dtype=np.int64)
-        self._copy_many = pa.lib().pa_copy_many
+        dst = [t.data_ptr() for t in bufs]
+        row_bytes = [t[0].numel() * t.element_size() for t in bufs]
         self._bucket_of = [self.bucket(n) for n in range(bmax + 1)]
+        self._descs, self._desc_rows = [], []
+        for n in range(bmax + 1):
+            d = pa.copy_descs(6)
+            v = np.frombuffer(d, dtype=np.int64).reshape(6, 3)
+            b = self._bucket_of[n] or n
+            v[:5, 1] = dst
+            v[:5, 2] = [n * r for r in row_bytes]
+            v[5] = (0, dst[4] + 4 * n, 4 * (b - n))
+            self._descs.append(d)
+            self._desc_rows.append(v)
+        self._copy_many = pa.lib().pa_copy_many
         self._out_rows = [self.out[:n] for n in range(bmax + 1)]
         self._width = max_blocks_per_seq
         # The staging goes to the stream the replay will run on (torch's current stream);
@@ -168,12 +177,8 @@ class GraphedDecode:
         srcs = (q, k_new, v_new, block_table, context_lens)
         if block_table.shape[1] != self._width or not all(t.is_contiguous() for t in srcs):
             return self._step_torch(q, k_new, v_new, block_table, context_lens, n, b)
-        rows = self._desc_rows
-        rows[:5, 0] = [t.data_ptr() for t in srcs]
-        rows[:5, 2] = self._row_bytes * n
-        # padding rows: no keys, no cache write
-        rows[5] = (0, rows[4, 1] + 4 * n, 4 * (b - n))
-        st = self._copy_many(self._descs, 6, self._raw_stream(self._device))
+        self._desc_rows[n][:5, 0] = [t.data_ptr() for t in srcs]
+        st = self._copy_many(self._descs[n], 6, self._raw_stream(self._device))
         if st:
             pa._check("pa_copy_many", st)
         self._padded(n, b)
