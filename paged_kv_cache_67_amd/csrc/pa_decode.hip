@@ -106,7 +106,11 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_kernel(
     st.store_final(out, (int64_t)b * HQ + h0);
 }
 
-// Standalone balanced kernel: grid = (slice, head group), one head wave per wave.
+// Standalone balanced kernel: wave item i of the grid runs slice i / head_waves of head
+// wave i % head_waves (head_waves = KV heads x query-head tiles per KV head).  Workgroups
+// hold max_head_waves(G) waves whatever the number of head waves, so that the grid is
+// about one workgroup per compute unit and every unit runs the same number of waves
+// (with one workgroup per slice, 4 head waves made 4-wave workgroups, 1.5 per unit).
 template <int D, int ET, int G>
 __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel(
     void* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_m,
@@ -114,11 +118,12 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel
     const void* __restrict__ kcache, const void* __restrict__ vcache,
     const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ context_lens,
     int B, int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt) {
-  const int hw = blockIdx.y * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int head_waves = HKV * (group / G);
+  const int item = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   decode_balanced_body<D, ET, G, false>(
-      blockIdx.x, hw, blockIdx.x == 0 && blockIdx.y == 0, out, ws_acc, ws_m, ws_l, ws_cuc, qptr,
-      kcache, vcache, block_table, maxb, context_lens, nullptr, nullptr, 0, B, num_blocks, bs_log2,
-      HQ, HKV, group, scale_log2, Wt);
+      item / head_waves, item % head_waves, blockIdx.x == 0, out, ws_acc, ws_m, ws_l, ws_cuc,
+      qptr, kcache, vcache, block_table, maxb, context_lens, nullptr, nullptr, 0, B, num_blocks,
+      bs_log2, HQ, HKV, group, scale_log2, Wt);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,7 +260,10 @@ static int launch_decode(const char* fn, const DecodePlan& pl, void* out, const 
   const WsPtrs w = pl.mode == DecodePlan::kSingle ? WsPtrs{} : carve(workspace, pl, B, HQ, D);
   if (pl.mode == DecodePlan::kBalanced) {
     const size_t lds = (size_t)(2 * B + 1) * sizeof(int);
-    hipLaunchKernelGGL(bkern, dim3(pl.Wt, groups), dim3(wpb * 64), lds, s, out, w.acc, w.m, w.l,
+    const int wpg = max_head_waves(pl.G);
+    const int64_t n_wg = ceil_div((int64_t)pl.Wt * head_waves, wpg);
+    if (n_wg > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: grid too large", fn);
+    hipLaunchKernelGGL(bkern, dim3((unsigned)n_wg), dim3(wpg * 64), lds, s, out, w.acc, w.m, w.l,
                        w.cuc, q, k_cache, v_cache, block_table, maxb, context_lens, B, NB,
                        __builtin_ctz(bs), HQ, HKV, group, scale * kLog2e, pl.Wt);
   } else {
