@@ -205,14 +205,32 @@ def check_hand_example(ns):
 
 
 def check_cached_append(ns):
+    """[Lab] B.1.2 printed run of the three-position example: after one vector is appended,
+    a single new query reading the cached K/V (4 KV positions, 1 query) gives the last
+    output of a full recomputation over all 4 positions with max error 0.0.  That equality
+    is what the page fixes, and it holds whatever the appended vector is, so it is checked
+    here for several vectors (decode of the new query over the paged cache against the last
+    row of a causal prefill of all four positions, in the same precision).  The page also
+    prints that last output, [0.6304, 0.8374], but not the appended vector: the value check
+    uses the one vector that reproduces it (reading R20) and is secondary to the equality."""
     g = golden("lab_b1_attention.json")
     x = np.array(g["causal_qkv_equal"]["x"])
-    y = np.vstack([x, [g["cached_append"]["appended_reading"]]]).astype(np.float32)
-    q = y[-1][None, None, :]
-    out = _decode_contig(ns, q, [y[:, None, :]], [y[:, None, :]],
-                         g["causal_qkv_equal"]["scale"], 2, np.random.default_rng(3))
+    sc = g["causal_qkv_equal"]["scale"]
     c = g["cached_append"]
-    assert np.allclose(out[0, 0], c["last_output"], atol=c["abs_tol"], rtol=0), out
+    rng = np.random.default_rng(3)
+    appended = [c["appended_reading"]] + [list(rng.normal(0.0, 2.0, 2)) for _ in range(4)]
+    for a in appended:
+        y = np.vstack([x, [a]]).astype(np.float32)
+        cached = _decode_contig(ns, y[-1][None, None, :], [y[:, None, :]], [y[:, None, :]], sc, 2,
+                                np.random.default_rng(7))
+        full, _ = _prefill_contig(ns, [y[:, None, :]], [y[:, None, :]], [y[:, None, :]], [4], sc, 2,
+                                  np.random.default_rng(8))
+        assert full.shape[0] == c["query_positions_full"] == c["kv_positions"] == len(y)
+        assert cached.shape[:2] == (c["query_positions_cached"], 1)  # one query, one head
+        err = np.max(np.abs(cached[0, 0] - full[-1, 0]))
+        assert abs(err - c["max_error"]) <= c["max_error_tol"], (a, cached[0, 0], full[-1, 0])
+        if a is c["appended_reading"]:
+            assert np.allclose(cached[0, 0], c["last_output"], atol=c["abs_tol"], rtol=0), cached
 
 
 def _sdpa_decode(q, K, V, scale, HQ):
