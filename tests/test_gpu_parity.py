@@ -364,6 +364,21 @@ def test_decode_balanced_mixed_lengths(case):
     assert_close(out_f64(out, dtype), want, dtype, str(case[:5]))
 
 
+@pytest.mark.parametrize("B", [8192, 8193])
+def test_decode_at_the_balanced_batch_bound(B):
+    """The balanced split takes batches of up to 8192 sequences (its length scan keeps two
+    ints per sequence in LDS); a batch of 8193 takes the fixed-partition plan instead.  Both
+    sides of the bound, Qwen2.5-0.5B heads with short contexts, every row against the
+    oracle."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 40, size=B, endpoint=True).astype(np.int32)
+    w = make_workload(name=f"decode-b{B}", kind="decode", dtype="bf16", num_q_heads=14,
+                      num_kv_heads=2, head_dim=64, block_size=16, seq_lens_k=lens, seed=B % 997)
+    announce(f"decode at the balanced batch bound: B={B}")
+    dw = run_hip(w, partition_size=0)
+    assert_close(out_f64(dw.out, "bf16"), OracleRun(w).decode(), "bf16", f"B={B}")
+
+
 @pytest.mark.parametrize("partition", [0, 64])
 def test_decode_two_passes_equal_one_call(partition):
     """pa_decode_partitions + pa_decode_merge give exactly pa_decode's output."""
@@ -426,6 +441,25 @@ def test_mixed_full_chip_split(num_decode, num_prefill):
     dw = _mixed_run(w)
     assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(True), "bf16",
                  f"{num_decode} + {num_prefill}")
+
+
+@pytest.mark.parametrize("HQ,HKV,D,nseq", [(16, 8, 128, 2046), (14, 2, 64, 7507)])
+def test_mixed_at_the_lds_sequence_bound(HQ, HKV, D, nseq):
+    """The largest batch pa_attention_mixed takes: its length scan fills the workgroup's
+    LDS to the last byte beside the prefill tiles (2046 sequences at head_dim 128, 7507 at
+    64; one more is refused on the host).  Short decode rows and three prompt chunks, every
+    row against the oracle."""
+    rng = np.random.default_rng(nseq)
+    lk = rng.integers(1, 24, size=nseq, endpoint=True).astype(np.int32)
+    lq = np.ones(nseq, np.int32)
+    lk[:3] = [300, 129, 64]
+    lq[:3] = [100, 129, 64]
+    w = make_workload(name=f"mixed-{nseq}", kind="prefill", dtype="bf16", num_q_heads=HQ,
+                      num_kv_heads=HKV, head_dim=D, block_size=16, seq_lens_k=lk, new_lens=lq,
+                      seed=nseq % 991)
+    announce(f"mixed at the LDS bound: {nseq} sequences, d{D}")
+    dw = _mixed_run(w)
+    assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(True), "bf16", f"{nseq} seqs")
 
 
 def test_mixed_all_prefill_equals_prefill_kernel():
