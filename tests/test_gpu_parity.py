@@ -101,6 +101,16 @@ def test_decode_qwen3_full_size():
     assert_close(got, want, w.dtype, "cfg2")
 
 
+def test_decode_qwen3_full_size_single_pass():
+    """The benchmarked configuration with the split turned off (partition_size -1: one
+    pass, one wave per (sequence, head tile) over all its keys, no workspace): every row
+    against the oracle."""
+    w = config(2)
+    announce("decode cfg2 full size, single pass, all 256 rows")
+    dw = run_hip(w, partition_size=-1, with_workspace=False)
+    assert_close(out_f64(dw.out, w.dtype), oracle_run(2).decode(), w.dtype, "cfg2 P=1")
+
+
 @pytest.mark.parametrize("idx,parts", [(1, [16, 64, 256, 1024, -1]), (3, [256, 1024, 8192, -1])])
 def test_decode_any_partition_size(idx, parts):
     w = config(idx)
