@@ -74,8 +74,7 @@ def time_decode(args):
     log(f"sum(ctx)={int(w.seq_lens_k.sum())} partition={P} split={split}")
 
     def step(ev=None):
-        dw.slot_mapping()
-        dw.store()
+        dw.store_paged()  # a1 slot addressing + a2 scatter, one launch
         if ev is not None:
             ev[0].record()
         if split:
@@ -109,7 +108,8 @@ def time_decode(args):
 
     # component times, each in a loop of its own (not part of the reported step time)
     comp = {}
-    for name, fn in (("slot_mapping", dw.slot_mapping), ("store", dw.store)):
+    for name, fn in (("store_paged", dw.store_paged), ("slot_mapping", dw.slot_mapping),
+                     ("store", dw.store)):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(50):
@@ -272,8 +272,7 @@ def time_graphs(w, dw, args):
         ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
 
         def eager():
-            pk.pa_slot_mapping(slots, bt, cu, ctx, w.block_size, w.num_blocks)
-            pk.pa_store_kv(kn, vn, dw.k_cache, dw.v_cache, slots)
+            pk.pa_store_kv_paged(kn, vn, dw.k_cache, dw.v_cache, bt, cu, ctx, 1, slots)
             pk.pa_decode(out, q, dw.k_cache, dw.v_cache, bt, ctx, w.scale,
                          max_context_len=w.max_seqlen_k, partition_size=0, workspace=ws)
 
@@ -749,7 +748,7 @@ def main():
             "context_lens": "uniform [128, 4096], seed 67002",
             "sum_context_tokens": int(w.seq_lens_k.sum()),
             "split": {0: "balanced split-K", -1: "single pass"}.get(P, f"fixed {P}-token partitions"),
-            "step": "pa_slot_mapping + pa_store_kv + pa_decode_partitions + pa_decode_merge",
+            "step": "pa_store_kv_paged (slot addressing + store) + pa_decode_partitions + pa_decode_merge",
             "step_bytes": int(step_bytes),
         },
         "roofline": {

@@ -137,6 +137,35 @@ int pa_store_kv(const void* key, const void* value, int64_t key_token_stride,
                 void* stream);
 
 /*
+ * pa_store_kv_paged -- pa_slot_mapping followed by pa_store_kv, in one launch.
+ *
+ * The same slots as pa_slot_mapping ([KVblog] 3.5: slot = block_table[p / B] *
+ * B + p % B for the new token at position p = seq_lens_k[b] - Lq + i, -1 for
+ * a token whose logical block is unmapped) and the same scatter as
+ * pa_store_kv ([MinivLLM] store_kvcache_kernel), bit for bit; each token's
+ * row loads are in flight while its table entry is read, so the step's store
+ * costs one launch and one table round trip instead of two of each.
+ *
+ *   key, value, key_token_stride, value_token_stride   as for pa_store_kv
+ *   block_table, max_blocks_per_seq, cu_seqlens_q, seq_lens_k, num_seqs,
+ *   num_tokens, block_size, num_blocks                  as for pa_slot_mapping
+ *   max_seqlen_q  largest Lq of the batch (1 for decode); it sizes the grid
+ *                 only, a longer sequence is still stored whole
+ *   slot_mapping  out  int32 [num_tokens], or NULL: the slots computed, as
+ *                      pa_slot_mapping writes them
+ *
+ * Two tokens must not map to one slot.  Errors as for the two calls it
+ * replaces; num_seqs = 0 or num_tokens = 0 is a no-op.
+ */
+int pa_store_kv_paged(const void* key, const void* value, int64_t key_token_stride,
+                      int64_t value_token_stride, void* k_cache, void* v_cache,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, int32_t num_seqs,
+                      int32_t num_tokens, int32_t max_seqlen_q, int32_t num_blocks,
+                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                      int32_t* slot_mapping, void* stream);
+
+/*
  * Split-K (flash-decoding) for decode.
  *
  * A long context is split into pieces; each piece produces the online-softmax
@@ -428,15 +457,18 @@ int pa_read_ceiling(const void* k_cache, const void* v_cache, const int32_t* blo
  * Each drains `stream`, copies the metadata to the host and checks it there:
  * for debugging and tests, not for the hot path (it synchronises, so it
  * cannot be captured in a graph).  When the checks are switched on, the
- * matching check runs at the start of pa_store_kv, pa_decode,
- * pa_decode_partitions, pa_prefill_paged and pa_attention_mixed, which then
- * return its status instead of launching.  They start switched on when the
- * environment variable PA_DEBUG_CHECKS is set to anything but "0" at the
- * first call that looks; pa_set_debug_checks(on) switches them for the whole
- * process and returns the previous setting (0 / 1).
+ * matching check runs at the start of pa_store_kv, pa_store_kv_paged,
+ * pa_decode, pa_decode_partitions, pa_prefill_paged and pa_attention_mixed,
+ * which then return its status instead of launching.  They start switched on
+ * when the environment variable PA_DEBUG_CHECKS is set to anything but "0" at
+ * the first call that looks; pa_set_debug_checks(on) switches them for the
+ * whole process and returns the previous setting (0 / 1).
  *
  * pa_check_store_inputs: every slot_mapping entry is -1 or in
  *   [0, num_blocks*block_size), and no slot appears twice.
+ * pa_check_store_paged_inputs: cu_seqlens_q never decreases and lies within
+ *   [0, num_tokens], and no two new tokens map to one slot (the slots
+ *   pa_store_kv_paged computes).
  * pa_check_decode_inputs: 0 <= context_lens[b] <= max_context_len (or
  *   max_blocks_per_seq*block_size when max_context_len <= 0, and never
  *   above it), and the first ceil(context_lens[b]/block_size) block ids of
@@ -455,6 +487,10 @@ int pa_read_ceiling(const void* k_cache, const void* v_cache, const int32_t* blo
 int pa_set_debug_checks(int on);
 int pa_check_store_inputs(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                           int32_t block_size, void* stream);
+int pa_check_store_paged_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_blocks,
+                                int32_t block_size, void* stream);
 int pa_check_decode_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                            int32_t num_blocks, int32_t block_size, void* stream);

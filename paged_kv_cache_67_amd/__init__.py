@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     pa_check_decode_inputs,
     pa_check_prefill_inputs,
     pa_check_store_inputs,
+    pa_check_store_paged_inputs,
     pa_copy_blocks,
     pa_copy_many,
     pa_read_ceiling,
@@ -35,5 +36,6 @@ from ._binding import (  # noqa: F401
     pa_slot_mapping,
     pa_status_string,
     pa_store_kv,
+    pa_store_kv_paged,
     pa_version,
 )

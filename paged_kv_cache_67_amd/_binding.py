@@ -40,6 +40,8 @@ SIGNATURES = {
     "pa_slot_mapping": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_store_kv": (C.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                               C.c_int, _vp]),
+    "pa_store_kv_paged": (C.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                    _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp, _vp]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                             _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
@@ -60,6 +62,7 @@ SIGNATURES = {
                                   _vp, _vp]),
     "pa_set_debug_checks": (C.c_int, [C.c_int]),
     "pa_check_store_inputs": (C.c_int, [_vp, _i32, _i32, _i32, _vp]),
+    "pa_check_store_paged_inputs": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_check_decode_inputs": (C.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
     "pa_check_prefill_inputs": (C.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _vp]),
@@ -170,6 +173,29 @@ def pa_store_kv(key, value, k_cache, v_cache, slot_mapping, stream=None):
     _check("pa_store_kv", lib().pa_store_kv(
         _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_cache), _ptr(v_cache),
         _ptr(slot_mapping), N, NB, BS, HKV, D, _dtype(k_cache), _stream(stream)))
+
+
+def pa_store_kv_paged(key, value, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k,
+                      max_seqlen_q, slot_mapping=None, stream=None):
+    """pa_slot_mapping followed by pa_store_kv in one launch; slot_mapping, if given,
+    receives the slots."""
+    NB, BS, HKV, D = k_cache.shape
+    assert v_cache.shape == k_cache.shape and k_cache.is_contiguous() and v_cache.is_contiguous()
+    for t in (key, value):
+        assert t.dim() == 3 and t.shape[1:] == (HKV, D) and t.stride(2) == 1 and t.stride(1) == D
+        assert t.dtype == k_cache.dtype
+    assert value.shape[0] == key.shape[0]
+    B, maxb = block_table.shape
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    _i32_vec(cu_seqlens_q, B + 1, "cu_seqlens_q")
+    _i32_vec(seq_lens_k, B, "seq_lens_k")
+    N = key.shape[0]
+    if slot_mapping is not None:
+        _i32_vec(slot_mapping, N, "slot_mapping")
+    _check("pa_store_kv_paged", lib().pa_store_kv_paged(
+        _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), maxb, _ptr(cu_seqlens_q), _ptr(seq_lens_k), B, N, int(max_seqlen_q),
+        NB, BS, HKV, D, _dtype(k_cache), _ptr(slot_mapping), _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
@@ -286,6 +312,19 @@ def pa_check_store_inputs(slot_mapping, num_blocks, block_size, stream=None):
     _i32_vec(slot_mapping, slot_mapping.shape[0], "slot_mapping")
     _check("pa_check_store_inputs", lib().pa_check_store_inputs(
         _ptr(slot_mapping), slot_mapping.shape[0], num_blocks, block_size, _stream(stream)))
+
+
+def pa_check_store_paged_inputs(block_table, cu_seqlens_q, seq_lens_k, num_tokens, num_blocks,
+                                block_size, stream=None):
+    """Debug check of a fused store's offsets and the slots it computes (synchronises):
+    raises PAError naming the first decreasing offset or the first slot two tokens map to."""
+    B = block_table.shape[0]
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+    _i32_vec(cu_seqlens_q, B + 1, "cu_seqlens_q")
+    _i32_vec(seq_lens_k, B, "seq_lens_k")
+    _check("pa_check_store_paged_inputs", lib().pa_check_store_paged_inputs(
+        _ptr(block_table), block_table.shape[1], _ptr(cu_seqlens_q), _ptr(seq_lens_k), B,
+        int(num_tokens), num_blocks, block_size, _stream(stream)))
 
 
 def pa_check_decode_inputs(block_table, context_lens, num_blocks, block_size, max_context_len=0,

@@ -3,7 +3,7 @@
 // kernels never need these (they stay in bounds whatever the metadata holds); they name
 // the first broken rule of a batch, for debugging and tests.  With the checks switched on
 // (PA_DEBUG_CHECKS set to anything but "0" in the environment when the library first looks,
-// or pa_set_debug_checks(1)), pa_store_kv, pa_decode, pa_decode_partitions,
+// or pa_set_debug_checks(1)), pa_store_kv, pa_store_kv_paged, pa_decode, pa_decode_partitions,
 // pa_prefill_paged and pa_attention_mixed run them before every launch, which synchronises
 // the stream and so cannot be captured in a graph.
 #include <stdint.h>
@@ -92,6 +92,46 @@ int pa_check_store_inputs(const int32_t* slot_mapping, int32_t num_tokens, int32
                   (long long)nslots);
     if (!seen.insert(s).second)
       return fail(PA_ERR_CONTRACT, "%s: slot %d appears twice (token %d)", what, s, t);
+  }
+  return PA_OK;
+}
+
+int pa_check_store_paged_inputs(const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                int32_t num_seqs, int32_t num_tokens, int32_t num_blocks,
+                                int32_t block_size, void* stream) {
+  clear_error();
+  const char* what = "pa_check_store_paged_inputs";
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0 || num_blocks < 0 ||
+      block_size <= 0 || (block_size & (block_size - 1)))
+    return fail(PA_ERR_SHAPE, "%s: bad sizes", what);
+  if (num_seqs > 0 && (!block_table || !cu_seqlens_q || !seq_lens_k))
+    return fail(PA_ERR_NULL, "%s: null pointer", what);
+  if (num_seqs == 0) return PA_OK;
+  std::vector<int32_t> cq, lk, bt;
+  hipStream_t s = (hipStream_t)stream;
+  if (int st = fetch(cq, cu_seqlens_q, num_seqs + 1, s, what)) return st;
+  if (int st = fetch(lk, seq_lens_k, num_seqs, s, what)) return st;
+  if (int st = fetch(bt, block_table, (int64_t)num_seqs * max_blocks_per_seq, s, what)) return st;
+  if (cq[0] < 0 || cq[num_seqs] > num_tokens)
+    return fail(PA_ERR_CONTRACT, "%s: cu_seqlens_q spans [%d, %d], outside [0, %d]", what, cq[0],
+                cq[num_seqs], num_tokens);
+  // The slots the store writes, as the kernel computes them (-1 for a token whose logical
+  // block is unmapped): no two tokens may write one slot.
+  std::unordered_set<int64_t> seen;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t lq = cq[b + 1] - cq[b];
+    if (lq < 0) return fail(PA_ERR_CONTRACT, "%s: cu_seqlens_q decreases at sequence %d", what, b);
+    for (int32_t i = 0; i < lq; ++i) {
+      const int64_t p = (int64_t)lk[b] - lq + i;
+      if (p < 0 || p / block_size >= max_blocks_per_seq) continue;
+      const int32_t blk = bt[(size_t)b * max_blocks_per_seq + p / block_size];
+      if (blk < 0 || blk >= num_blocks) continue;
+      const int64_t slot = (int64_t)blk * block_size + p % block_size;
+      if (!seen.insert(slot).second)
+        return fail(PA_ERR_CONTRACT, "%s: slot %lld written twice (sequence %d, token %d)", what,
+                    (long long)slot, b, cq[b] + i);
+    }
   }
   return PA_OK;
 }

@@ -54,6 +54,47 @@ __global__ __launch_bounds__(256) void store_kv_kernel(
   }
 }
 
+// a1 and a2 in one launch.  blockIdx.y strides over the sequences and blockIdx.x x threads
+// over the sequence's (new token, 16-byte chunk) items.  Each item computes its token's
+// slot as slot_mapping_kernel does (every chunk of a row reads the same lengths and table
+// entry, served from cache) and copies its chunk of the K and V rows.  The row loads
+// depend only on the token index, so they are in flight while the table entry is read,
+// instead of waiting for a separate slot pass and its reread of the slots.
+__global__ __launch_bounds__(256) void store_kv_paged_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, int64_t key_stride_bytes,
+    int64_t value_stride_bytes, char* __restrict__ kc, char* __restrict__ vc,
+    const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ lens_k, int num_seqs, int num_tokens, int bs_log2,
+    int num_blocks, int row_chunks, int64_t row_bytes, int32_t* __restrict__ slots_out) {
+  const int bs = 1 << bs_log2;
+  for (int b = blockIdx.y; b < num_seqs; b += gridDim.y) {
+    const int q0 = cu_q[b];
+    const int lq = cu_q[b + 1] - q0;
+    const int lk = lens_k[b];
+    const int32_t* row = block_table + (int64_t)b * maxb;
+    const int64_t items = (int64_t)(lq > 0 ? lq : 0) * row_chunks;
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
+         it += (int64_t)gridDim.x * blockDim.x) {
+      const int i = int(it / row_chunks);
+      const int c = int(it - (int64_t)i * row_chunks);
+      const int t = q0 + i;
+      if (t < 0 || t >= num_tokens) continue;
+      const uint4 k = reinterpret_cast<const uint4*>(key + (int64_t)t * key_stride_bytes)[c];
+      const uint4 v = reinterpret_cast<const uint4*>(value + (int64_t)t * value_stride_bytes)[c];
+      const int p = lk - lq + i;
+      int s = -1;
+      if (p >= 0 && (p >> bs_log2) < maxb) {
+        const int blk = row[p >> bs_log2];
+        if (blk >= 0 && blk < num_blocks) s = blk * bs + (p & (bs - 1));
+      }
+      if (slots_out && c == 0) slots_out[t] = s;
+      if (s < 0) continue;
+      reinterpret_cast<uint4*>(kc + (int64_t)s * row_bytes)[c] = k;
+      reinterpret_cast<uint4*>(vc + (int64_t)s * row_bytes)[c] = v;
+    }
+  }
+}
+
 // Whole-block copy of both pools for a list of (src, dst) block pairs.  blockIdx.y strides
 // over the pairs, blockIdx.x x threads over the 16-byte chunks of one block; a pair with an
 // id out of range, or src == dst, copies nothing.
@@ -205,6 +246,58 @@ extern "C" int pa_store_kv(const void* key, const void* value, int64_t key_token
                      value_token_stride * eb, (char*)k_cache, (char*)v_cache, slot_mapping, items,
                      row_chunks, (int64_t)num_blocks * block_size, row_bytes);
   return check_launch("pa_store_kv");
+}
+
+extern "C" int pa_store_kv_paged(const void* key, const void* value, int64_t key_token_stride,
+                                 int64_t value_token_stride, void* k_cache, void* v_cache,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t max_seqlen_q,
+                                 int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                 int32_t head_dim, pa_dtype dtype, int32_t* slot_mapping,
+                                 void* stream) {
+  clear_error();
+  const char* fn = "pa_store_kv_paged";
+  if (num_seqs < 0 || num_tokens < 0 || max_seqlen_q < 0 || max_blocks_per_seq < 0 ||
+      num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PA_ERR_SHAPE, "%s: bad sizes", fn);
+  if (dtype != PA_F32 && dtype != PA_BF16 && dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
+  if (!is_pow2(block_size) || block_size < 8 || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d not a power of two in [8,1024]", fn,
+                block_size);
+  if ((int64_t)num_blocks * block_size > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "%s: num_blocks*block_size exceeds int32 slots", fn);
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (max_blocks_per_seq == 0) return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq is 0", fn);
+  if (!key || !value || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !seq_lens_k)
+    return fail(PA_ERR_NULL, "%s: null pointer", fn);
+  const int eb = elt_bytes(dtype);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * eb;
+  if (key_token_stride < (int64_t)num_kv_heads * head_dim ||
+      value_token_stride < (int64_t)num_kv_heads * head_dim)
+    return fail(PA_ERR_SHAPE, "%s: token stride smaller than a row", fn);
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16 ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 3u))
+    return fail(PA_ERR_ALIGN, "%s: pointers and token strides must be 16-byte aligned", fn);
+  if (debug_checks())
+    if (int cs = pa_check_store_paged_inputs(block_table, max_blocks_per_seq, cu_seqlens_q,
+                                             seq_lens_k, num_seqs, num_tokens, num_blocks,
+                                             block_size, stream))
+      return cs;
+  const int row_chunks = int(row_bytes / 16);
+  const int64_t per_seq = (int64_t)(max_seqlen_q > 0 ? max_seqlen_q : 1) * row_chunks;
+  const int64_t gx = (per_seq + 255) / 256;
+  const dim3 grid(unsigned(gx < 1024 ? gx : 1024), unsigned(num_seqs < 65535 ? num_seqs : 65535));
+  hipLaunchKernelGGL(store_kv_paged_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     (const char*)key, (const char*)value, key_token_stride * eb,
+                     value_token_stride * eb, (char*)k_cache, (char*)v_cache, block_table,
+                     max_blocks_per_seq, cu_seqlens_q, seq_lens_k, num_seqs, num_tokens,
+                     __builtin_ctz(block_size), num_blocks, row_chunks, row_bytes, slot_mapping);
+  return check_launch(fn);
 }
 
 extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,

@@ -107,9 +107,9 @@ class GraphedDecode:
         return self.buckets[i] if i < len(self.buckets) else None
 
     def _launch(self, b):
-        pa.pa_slot_mapping(self.slots[:b], self.block_table[:b], self.cu_q[:b + 1],
-                           self.context_lens[:b], self.block_size, self.num_blocks)
-        pa.pa_store_kv(self.k_new[:b], self.v_new[:b], self.k_cache, self.v_cache, self.slots[:b])
+        pa.pa_store_kv_paged(self.k_new[:b], self.v_new[:b], self.k_cache, self.v_cache,
+                             self.block_table[:b], self.cu_q[:b + 1], self.context_lens[:b], 1,
+                             self.slots[:b])
         pa.pa_decode(self.out[:b], self.q[:b], self.k_cache, self.v_cache, self.block_table[:b],
                      self.context_lens[:b], self.scale, max_context_len=self.max_context_len,
                      partition_size=0, workspace=self.workspace)
@@ -129,10 +129,9 @@ class GraphedDecode:
         """The same step launched directly on the caller's tensors (no graph)."""
         n = q.shape[0]
         dev = q.device
-        slots = torch.empty(n, dtype=torch.int32, device=dev)
         cu_q = torch.arange(n + 1, dtype=torch.int32, device=dev)
-        pa.pa_slot_mapping(slots, block_table, cu_q, context_lens, self.block_size, self.num_blocks)
-        pa.pa_store_kv(k_new, v_new, self.k_cache, self.v_cache, slots)
+        pa.pa_store_kv_paged(k_new, v_new, self.k_cache, self.v_cache, block_table, cu_q,
+                             context_lens, 1)
         out = torch.empty_like(q)
         nbytes = pa.pa_decode_workspace_size(n, q.shape[1], self.k_cache.shape[2], q.shape[2],
                                              self.max_context_len, 0)

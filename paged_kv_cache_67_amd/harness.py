@@ -89,6 +89,13 @@ class DeviceWorkload:
     def store(self, stream=None):
         pa.pa_store_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.slots_new, stream)
 
+    def store_paged(self, stream=None, write_slots=True):
+        """slot_mapping and store in one launch (pa_store_kv_paged)."""
+        w = self.w
+        pa.pa_store_kv_paged(self.k_new, self.v_new, self.k_cache, self.v_cache, self.block_table,
+                             self.cu_q, self.seq_lens_k, max(1, w.max_seqlen_q),
+                             self.slots_new if write_slots else None, stream)
+
     def attention(self, stream=None):
         w = self.w
         if w.kind == "decode":

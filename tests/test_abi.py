@@ -74,6 +74,19 @@ def test_null_and_shape_errors(L):
     assert L.pa_store_kv(None, None, 128, 128, None, None, None, 4, 8, 16, 2, 64, 7, None) == 3
     assert L.pa_store_kv(None, None, 128, 128, None, None, None, 0, 8, 16, 2, 64, 1, None) == 0
     assert L.pa_slot_mapping(None, None, 4, None, None, 2, 2, 16, 8, None) == 1
+    # pa_store_kv_paged: (key, value, strides, pools, table, maxb, cu_q, lens, seqs, tokens,
+    # max_seqlen_q, blocks, block_size, kv_heads, dim, dtype, slots out, stream)
+    paged = lambda seqs, toks, mq, bs, d, dt: L.pa_store_kv_paged(
+        None, None, 128, 128, None, None, None, 4, None, None, seqs, toks, mq, 8, bs, 2, d, dt,
+        None, None)
+    assert paged(2, 2, 1, 16, 64, 1) == 1          # null pointers
+    assert paged(2, 2, 1, 16, 64, 7) == 3          # dtype
+    assert paged(2, 2, 1, 24, 64, 1) == 3          # block size not a power of two
+    assert paged(2, 2, 1, 16, 96, 1) == 3          # head_dim
+    assert paged(-1, 2, 1, 16, 64, 1) == 2
+    assert paged(2, 2, -1, 16, 64, 1) == 2
+    assert paged(0, 0, 1, 16, 64, 1) == 0          # empty batch: no-op
+    assert paged(2, 0, 1, 16, 64, 1) == 0
     assert L.pa_slot_mapping(None, None, 4, None, None, 2, 2, 24, 8, None) == 3
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 8, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 0, None) == 3
     assert L.pa_prefill_paged(None, None, None, None, None, 4, None, None, 2, 9, 4, 8, 8, 16, 4, 2, 128, 0.1, 1, 1, None) == 2
@@ -110,6 +123,12 @@ def test_alignment_and_workspace_errors(L):
     mis = ctypes.c_void_p(0x10008)
     assert L.pa_store_kv(mis, a, 1024, 1024, a, a, a, 4, 8, 16, 8, 128, 1, None) == 4
     assert L.pa_store_kv(a, a, 1028, 1024, a, a, a, 4, 8, 16, 8, 128, 1, None) == 4
+    paged = lambda key, kstride, slots: L.pa_store_kv_paged(
+        key, a, kstride, 1024, a, a, a, 4, a, a, 2, 4, 2, 8, 16, 8, 128, 1, slots, None)
+    assert paged(mis, 1024, None) == 4
+    assert paged(a, 1028, None) == 4
+    assert paged(a, 1024, ctypes.c_void_p(0x10002)) == 4   # slot output not 4-byte aligned
+    assert paged(a, 1000, None) == 2                        # stride shorter than a row
     assert L.pa_decode(a, a, a, mis, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, None, 0, None) == 4
     # explicit split without enough workspace
     assert L.pa_decode(a, a, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 16, None, 0, None) == 5
@@ -225,6 +244,10 @@ def test_check_functions_host_validation(L):
     assert L.pa_check_store_inputs(None, -1, 4, 16, None) == 2
     assert L.pa_check_store_inputs(None, 3, 4, 16, None) == 1
     assert L.pa_check_store_inputs(None, 0, 4, 16, None) == 0
+    assert L.pa_check_store_paged_inputs(None, 4, None, None, -1, 2, 4, 16, None) == 2
+    assert L.pa_check_store_paged_inputs(None, 4, None, None, 2, 2, 4, 24, None) == 2
+    assert L.pa_check_store_paged_inputs(None, 4, None, None, 2, 2, 4, 16, None) == 1
+    assert L.pa_check_store_paged_inputs(None, 4, None, None, 0, 0, 4, 16, None) == 0
     assert L.pa_check_decode_inputs(None, 0, None, 1, 0, 4, 16, None) == 2
     assert L.pa_check_decode_inputs(None, 4, None, 2, 0, 4, 16, None) == 1
     assert L.pa_check_decode_inputs(None, 4, None, 0, 0, 4, 16, None) == 0

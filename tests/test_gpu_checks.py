@@ -90,6 +90,29 @@ def test_check_prefill_inputs():
     assert _status(e) == CONTRACT and "block_table[0][1] = 5" in str(e.value)
 
 
+def test_check_store_paged_inputs():
+    announce("pa_check_store_paged_inputs")
+    bt = _i32([[0, 1, -1], [2, -1, -1]])
+    # sequence 0: 2 new tokens at positions 18, 19 (block 1); sequence 1: 1 at position 4
+    pk.pa_check_store_paged_inputs(bt, _i32([0, 2, 3]), _i32([20, 5]), num_tokens=3,
+                                   num_blocks=3, block_size=16)
+    # unmapped tokens (a -1 entry, a position past the row) write nothing and pass
+    pk.pa_check_store_paged_inputs(bt, _i32([0, 2, 3]), _i32([20, 60]), num_tokens=3,
+                                   num_blocks=3, block_size=16)
+    with pytest.raises(pk.PAError) as e:  # both sequences' new tokens land in block 1, row 3
+        pk.pa_check_store_paged_inputs(_i32([[0, 1, -1], [1, -1, -1]]), _i32([0, 2, 3]),
+                                       _i32([20, 4]), num_tokens=3, num_blocks=3, block_size=16)
+    assert _status(e) == CONTRACT and "slot 19 written twice" in str(e.value), str(e.value)
+    with pytest.raises(pk.PAError) as e:
+        pk.pa_check_store_paged_inputs(bt, _i32([0, 2, 1]), _i32([20, 5]), num_tokens=3,
+                                       num_blocks=3, block_size=16)
+    assert _status(e) == CONTRACT and "decreases" in str(e.value)
+    with pytest.raises(pk.PAError) as e:
+        pk.pa_check_store_paged_inputs(bt, _i32([0, 2, 4]), _i32([20, 5]), num_tokens=3,
+                                       num_blocks=3, block_size=16)
+    assert _status(e) == CONTRACT and "outside [0, 3]" in str(e.value)
+
+
 @pytest.fixture()
 def checks_on():
     prev = pk.pa_set_debug_checks(True)
@@ -123,6 +146,14 @@ def test_entry_points_check_before_launch(checks_on):
     with pytest.raises(pk.PAError) as e:
         pk.pa_store_kv(dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, bad_slots)
     assert _status(e) == CONTRACT
+    twin_bt = dw.block_table.clone()
+    twin_bt[2] = twin_bt[0]  # sequences 0 and 2 (40 and 17 tokens) share blocks
+    twin_lens = dw.seq_lens_k.clone()
+    twin_lens[2] = 40  # so their new tokens map to one slot
+    with pytest.raises(pk.PAError) as e:
+        pk.pa_store_kv_paged(dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, twin_bt, dw.cu_q,
+                             twin_lens, 1, dw.slots_new)
+    assert _status(e) == CONTRACT and "written twice" in str(e.value)
 
     assert pk.pa_set_debug_checks(False)
     try:

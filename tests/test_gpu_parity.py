@@ -77,6 +77,67 @@ def test_store_skips_minus_one_and_strided_rows():
     assert bits_equal(harness.from_device(kc), kp) and bits_equal(harness.from_device(vc), vp)
 
 
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_fused_slots_and_store_bit_exact(idx):
+    """pa_store_kv_paged (slot addressing and the scatter in one launch): the oracle's slots
+    and both whole pools, bit for bit; with no slot output it writes the same pools and
+    leaves the slot buffer alone."""
+    w = config(idx)
+    ref = oracle_run(idx)
+    announce(f"fused store cfg{idx} {w.name} new={w.num_new_tokens}")
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    dw.store_paged()
+    torch.cuda.synchronize()
+    assert np.array_equal(dw.slots_new.cpu().numpy(), ref.slots_new)
+    assert bits_equal(harness.from_device(dw.k_cache), ref.k_pool)
+    assert bits_equal(harness.from_device(dw.v_cache), ref.v_pool)
+    dw2 = harness.DeviceWorkload(w, "cuda")
+    dw2.load_history()
+    dw2.slots_new.fill_(-7)
+    dw2.store_paged(write_slots=False)
+    torch.cuda.synchronize()
+    assert bool((dw2.slots_new == -7).all())
+    assert bits_equal(harness.from_device(dw2.k_cache), ref.k_pool)
+    assert bits_equal(harness.from_device(dw2.v_cache), ref.v_pool)
+
+
+def test_fused_store_unmapped_tokens_views_and_short_grid():
+    """pa_store_kv_paged with new tokens whose logical block is unmapped (a -1 table entry,
+    and a position past the table row): slot -1, nothing written; key and value are views
+    into a fused tensor; max_seqlen_q = 1 sizes the grid below the longest chunk, which is
+    still stored whole."""
+    w = make_workload(name="fused-edge", kind="prefill", dtype="bf16", num_q_heads=4,
+                      num_kv_heads=2, head_dim=64, block_size=16, seq_lens_k=[40, 300, 17, 33],
+                      new_lens=[3, 100, 1, 33], seed=43)
+    bt = w.block_table.copy()
+    bt[1, 12] = -1                 # positions 192..207 of sequence 1 (new tokens) unmapped
+    maxb = bt.shape[1]
+    lens = w.seq_lens_k.copy()
+    lens[3] = maxb * w.block_size + 5   # sequence 3's new tokens run past its table row
+    announce("fused store: unmapped tokens, fused-tensor views, short grid")
+    dev = "cuda"
+    HKV, D = w.num_kv_heads, w.head_dim
+    fused = torch.zeros(w.num_new_tokens, 3, HKV, D, dtype=torch.bfloat16, device=dev)
+    fused[:, 1] = harness.to_device(w.k_new, "bf16", dev)
+    fused[:, 2] = harness.to_device(w.v_new, "bf16", dev)
+    kc = torch.full(w.pool_shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = kc.clone()
+    slots = torch.full((w.num_new_tokens,), -7, dtype=torch.int32, device=dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    pk.pa_store_kv_paged(fused[:, 1], fused[:, 2], kc, vc, i32(bt), i32(w.cu_seqlens_q), i32(lens),
+                         1, slots)
+    torch.cuda.synchronize()
+    want = oracle.slot_mapping(bt, w.cu_seqlens_q, lens, w.block_size)
+    # sequence 1: its new positions 200..207 lie in the unmapped block; sequence 3: all 33
+    # new positions lie in -1 padding entries or past the row
+    assert (want == -1).sum() == 8 + 33
+    assert np.array_equal(slots.cpu().numpy(), want)
+    kp, vp = w.empty_pool(), w.empty_pool()
+    oracle.store_kv(kp, vp, w.k_new, w.v_new, want)
+    assert bits_equal(harness.from_device(kc), kp) and bits_equal(harness.from_device(vc), vp)
+
+
 # ---------------------------------------------------------------------------
 # a3 + a4: decode
 
