@@ -708,8 +708,9 @@ def main():
         oracle_all_cores(float(args.oracle_leg[0]), int(args.oracle_leg[1]))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: the paged-attention path needs no collective and this "
-              "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the paged-attention path needs no collective (a "
+              "multi-GPU run shards sequences or KV heads, each GPU running this same step on "
+              "its share); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
