@@ -368,6 +368,31 @@ def test_prefill_variants(case, causal):
     assert_close(out_f64(dw.out, "bf16"), OracleRun(w).prefill(causal), "bf16", str(case))
 
 
+def test_prefill_wide_blocks_past_the_lds_window():
+    """Blocks of 128 tokens (one key tile per block, each tile's block located a step ahead
+    of its loads) with a table of 2101 blocks, longer than the kernel's 2048-entry LDS window:
+    the window slides, in pa_prefill_paged and in the mixed launch."""
+    w = make_workload(name="wide-window", kind="prefill", dtype="bf16", num_q_heads=2,
+                      num_kv_heads=1, head_dim=64, block_size=128,
+                      seq_lens_k=[2100 * 128 + 50, 300, 1], new_lens=[40, 100, 1], seed=57)
+    assert w.block_table.shape[1] > 2048
+    announce("prefill with 128-token blocks past the LDS window (2101 blocks)")
+    ref = OracleRun(w)
+    want = ref.prefill(True)
+    dw = harness.DeviceWorkload(w, "cuda")
+    dw.load_history()
+    dw.slot_mapping()
+    dw.store()
+    pk.pa_prefill_paged(dw.out, dw.q, dw.k_cache, dw.v_cache, dw.block_table, dw.cu_q, dw.cu_k,
+                        w.max_seqlen_q, w.max_seqlen_k, w.scale)
+    torch.cuda.synchronize()
+    assert_close(out_f64(dw.out, "bf16"), want, "bf16", "prefill")
+    dw.out.zero_()
+    dw.attention_mixed()
+    torch.cuda.synchronize()
+    assert_close(out_f64(dw.out, "bf16"), want, "bf16", "mixed")
+
+
 def test_prefill_future_change_bitwise():
     """Changing the K/V of the last chunk token leaves every earlier query row unchanged."""
     w = make_workload(name="future", kind="prefill", dtype="bf16", num_q_heads=16, num_kv_heads=8,
