@@ -251,24 +251,37 @@ __device__ __forceinline__ void prefill_body(
     toff[i] = 2u * (uint32_t)(trow[i] * HKVD + tcol[i]);
   }
   // A tile past the last one loads the last tile's keys (clamped to key nk - 1) and is
-  // never read.
+  // never read.  WIDE: a tile is one block's rows from a scalar base; its base and the
+  // count of valid rows after its first (lim) are found one step before the tile is
+  // issued (Tile, locate), so that the table lookup and the address arithmetic run beside
+  // the previous step's matrix work instead of holding up the step's first loads.
+  struct Tile {
+    const uint16_t* base;
+    int lim;
+  };
+  auto locate = [&](const uint16_t* src, int kt) __attribute__((always_inline)) {
+    const int ktc = min(kt, (ntiles - 1) * BN);
+    const int blk = __builtin_amdgcn_readfirstlane(lookup(ktc >> bs_log2));
+    return Tile{src + (((int64_t)blk << bs_log2) + (ktc & bs_mask)) * HKVD, nk - 1 - ktc};
+  };
+  auto issue_at = [&](const Tile& a, uint16_t* dst) __attribute__((always_inline)) {
+    const uint16_t* base = a.base;
+    const int lim = a.lim;
+    if (lim >= BN - 1) {  // a whole tile: no row clamps
+#pragma unroll
+      for (int i = 0; i < LPT; ++i)
+        load_to_lds(reinterpret_cast<const char*>(base) + toff[i],
+                    (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i)
+        load_to_lds(reinterpret_cast<const char*>(base) + (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])),
+                    (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
+    }
+  };
   auto issue = [&](const uint16_t* src, int kt, uint16_t* dst) __attribute__((always_inline)) {
     if constexpr (WIDE) {
-      const int ktc = min(kt, (ntiles - 1) * BN);
-      const int blk = __builtin_amdgcn_readfirstlane(lookup(ktc >> bs_log2));
-      const uint16_t* base = src + (((int64_t)blk << bs_log2) + (ktc & bs_mask)) * HKVD;
-      const int lim = nk - 1 - ktc;
-      if (lim >= BN - 1) {  // a whole tile: no row clamps
-#pragma unroll
-        for (int i = 0; i < LPT; ++i)
-          load_to_lds(reinterpret_cast<const char*>(base) + toff[i],
-                      (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
-      } else {
-#pragma unroll
-        for (int i = 0; i < LPT; ++i)
-          load_to_lds(reinterpret_cast<const char*>(base) + (uint32_t)(2 * (min(trow[i], lim) * HKVD + tcol[i])),
-                      (uint32_t)(uintptr_t)(dst + 512 * (wu + 8 * i)));
-      }
+      issue_at(locate(src, kt), dst);
     } else {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
@@ -334,11 +347,17 @@ __device__ __forceinline__ void prefill_body(
     tr_off[db] = tr_row * D + (((2 * db + ((lane & 3) >> 1)) ^ swz(tr_row)) * 8) + 4 * (lane & 1);
 
   f32x4_t sc[2][KB];  // scores of the tile being reduced
+  Tile next_v, next_k;  // WIDE: V_{t+1} and K_{t+2}, located during step t - 1
   auto step = [&](int t) __attribute__((always_inline)) {
     const int kt = t * BN;
     // V_{t+1} and K_{t+2} into the buffers step t - 1 finished reading.
-    issue_v(t + 1);
-    issue_k(t + 2);
+    if constexpr (WIDE) {
+      issue_at(next_v, sKV[2 + ((t + 1) & 1)]);
+      issue_at(next_k, sKV[t & 1]);
+    } else {
+      issue_v(t + 1);
+      issue_k(t + 2);
+    }
     if (kt + BN > nk_min) {
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg)
@@ -409,6 +428,15 @@ __device__ __forceinline__ void prefill_body(
       __builtin_amdgcn_sched_barrier(0);
     }
 
+    // The next step's tiles, located while this step's matrix work runs.  V_{t+2} lies in
+    // the block window the last slide left (it starts at or before K_{t+2}'s block); the
+    // window then moves for K_{t+3}.
+    if constexpr (WIDE) {
+      next_v = locate(vc, (t + 2) * BN);
+      cover((t + 3) * BN);
+      next_k = locate(kc, (t + 3) * BN);
+    }
+
     // O^T += V^T P^T, the transposing reads of d block db + 1 issued before the MFMAs of
     // block db (and the row-sum MFMAs covering the first reads).
     const uint16_t* V = sKV[2 + (t & 1)];
@@ -455,6 +483,11 @@ __device__ __forceinline__ void prefill_body(
     issue_k(0);
     issue_v(0);
     issue_k(1);
+    if constexpr (WIDE) {
+      next_v = locate(vc, BN);
+      cover(2 * BN);
+      next_k = locate(kc, 2 * BN);
+    }
     // Settle the Q loads here: the compiler does not count the tile loads, so this wait
     // also covers K_0, V_0 and K_1.
 #pragma unroll
