@@ -634,3 +634,52 @@ def test_prefill_and_mixed_random_shapes(seed):
     dw.attention_mixed()
     torch.cuda.synchronize()
     assert_close(out_f64(dw.out, c["dtype"]), want, c["dtype"], f"mixed {c}")
+
+
+def _random_decode_case(seed):
+    r = np.random.default_rng(seed)
+    G = int(r.choice([1, 2, 3, 4, 5, 6, 7, 8, 16]))
+    HKV = int(r.choice([1, 2, 4, 8])) if G < 16 else int(r.choice([1, 2]))
+    D = int(r.choice([64, 128]))
+    bs = int(r.choice([8, 16, 32, 64, 128, 256, 512]))
+    B = int(r.choice([1, 2, 3, 7, 33, 130, 300]))
+    mix = r.random()
+    if mix < 0.3:  # short rows, some empty
+        lens = r.integers(0, 40, size=B)
+    elif mix < 0.6:  # one long row among short ones
+        lens = r.integers(1, 64, size=B)
+        lens[int(r.integers(0, B))] = int(r.integers(2000, 9000))
+    else:
+        lens = r.integers(1, 2500, size=B)
+    dtype = str(r.choice(["bf16", "bf16", "f16", "f32"]))
+    P = int(r.choice([0, 0, 0, -1, 16, 64, 512]))
+    return dict(G=G, HKV=HKV, D=D, bs=bs, lens=lens.astype(np.int32).tolist(), dtype=dtype, P=P)
+
+
+@pytest.mark.parametrize("seed", list(range(40)))
+def test_decode_random_shapes(seed):
+    """Seeded random decode batches: GQA group 1-8 or 16, head_dim 64 / 128, block 8-512,
+    batch 1-300 with short, empty and long rows mixed, bf16 / fp16 / fp32, every partition
+    mode; every row against the oracle."""
+    c = _random_decode_case(2000 + seed)
+    lens = np.array(c["lens"], dtype=np.int32)
+    w = make_workload(name="rand-decode", kind="decode", dtype=c["dtype"],
+                      num_q_heads=c["G"] * c["HKV"], num_kv_heads=c["HKV"], head_dim=c["D"],
+                      block_size=c["bs"], seq_lens_k=np.maximum(lens, 1), seed=seed)
+    announce(f"random decode case {seed}: " + str({k: v for k, v in c.items() if k != "lens"}) +
+             f" B={len(lens)} max={int(lens.max())}")
+    dw = harness.DeviceWorkload(w, "cuda", partition_size=c["P"])
+    dw.load_history()
+    dw.step()
+    ctx = torch.from_numpy(lens).cuda()
+    out = torch.full_like(dw.out, float("nan"))
+    max_ctx = max(1, int(lens.max()))
+    nbytes = pk.pa_decode_workspace_size(len(lens), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         max_ctx, c["P"])
+    ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device="cuda") if nbytes else None
+    pk.pa_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_table, ctx, w.scale,
+                 max_context_len=max_ctx, partition_size=c["P"], workspace=ws)
+    torch.cuda.synchronize()
+    ref = OracleRun(w)
+    want = oracle.decode(w.q, ref.k_pool, ref.v_pool, w.block_table, lens, w.scale, c["dtype"])
+    assert_close(out_f64(out, c["dtype"]), want, c["dtype"], str(c))
