@@ -683,3 +683,48 @@ def test_decode_random_shapes(seed):
     ref = OracleRun(w)
     want = oracle.decode(w.q, ref.k_pool, ref.v_pool, w.block_table, lens, w.scale, c["dtype"])
     assert_close(out_f64(out, c["dtype"]), want, c["dtype"], str(c))
+
+
+@pytest.mark.parametrize("seed", list(range(20)))
+def test_store_random_tables(seed):
+    """Seeded random varlen batches with holes in the block tables (-1 entries inside and
+    past the live range): pa_slot_mapping + pa_store_kv and pa_store_kv_paged both give the
+    oracle's slots and both whole pools bit for bit."""
+    r = np.random.default_rng(3000 + seed)
+    HKV = int(r.choice([1, 2, 4, 8]))
+    D = int(r.choice([64, 128]))
+    bs = int(r.choice([8, 16, 64, 256]))
+    dtype = str(r.choice(["bf16", "f16", "f32"]))
+    B = int(r.integers(1, 9))
+    lk = r.integers(1, 600, size=B)
+    lq = np.array([int(r.integers(1, k + 1)) if r.random() < 0.5 else 1 for k in lk])
+    w = make_workload(name="rand-store", kind="prefill", dtype=dtype, num_q_heads=HKV,
+                      num_kv_heads=HKV, head_dim=D, block_size=bs, seq_lens_k=lk.tolist(),
+                      new_lens=lq.tolist(), seed=seed)
+    bt = w.block_table.copy()
+    holes = r.random(bt.shape) < 0.15
+    bt[holes] = -1
+    announce(f"random store case {seed}: HKV={HKV} D={D} bs={bs} {dtype} lk={lk.tolist()} "
+             f"lq={lq.tolist()} holes={int(holes.sum())}")
+    want = oracle.slot_mapping(bt, w.cu_seqlens_q, w.seq_lens_k, w.block_size)
+    kp, vp = w.empty_pool(), w.empty_pool()
+    oracle.store_kv(kp, vp, w.k_new, w.v_new, want)
+    dev = "cuda"
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    k_new, v_new = harness.to_device(w.k_new, dtype, dev), harness.to_device(w.v_new, dtype, dev)
+    for fused in (False, True):
+        kc = torch.full(w.pool_shape, float("nan"), dtype=tdt, device=dev)
+        vc = kc.clone()
+        slots = torch.full((w.num_new_tokens,), -7, dtype=torch.int32, device=dev)
+        if fused:
+            pk.pa_store_kv_paged(k_new, v_new, kc, vc, i32(bt), i32(w.cu_seqlens_q),
+                                 i32(w.seq_lens_k), int(lq.max()), slots)
+        else:
+            pk.pa_slot_mapping(slots, i32(bt), i32(w.cu_seqlens_q), i32(w.seq_lens_k), bs,
+                               w.num_blocks)
+            pk.pa_store_kv(k_new, v_new, kc, vc, slots)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), want), f"slots, fused={fused}"
+        assert bits_equal(harness.from_device(kc), kp) and bits_equal(harness.from_device(vc), vp), \
+            f"pools, fused={fused}"
