@@ -344,6 +344,8 @@ PREFILL_CASES = [
     (32, 4, 128, 64, [150, 260], [40, 130]),
     (16, 1, 128, 256, [513], [257]),
     (16, 8, 128, 128, [384, 200, 129], [128, 73, 129]),  # one key tile per block; ragged tails
+    (16, 8, 128, 512, [1300, 600, 513], [300, 64, 513]),   # several key tiles per block
+    (8, 2, 64, 1024, [2100, 1025, 40], [77, 1025, 40]),    # the largest block size
     # block tables longer than the kernel's LDS copy (2048 entries): the window slides
     (2, 1, 64, 8, [40000, 300], [40, 100]),
     (8, 2, 128, 8, [18000], [32]),
