@@ -504,6 +504,7 @@ MIXED_CASES = [
     (8, 4, 128, 128, [385, 129, 1, 640], [129, 1, 1, 128]),           # one key tile per block
     (8, 1, 128, 32, [700, 1, 333, 96, 2000], [200, 1, 1, 96, 1]),      # group 8: 4-head decode tiles
     (64, 8, 64, 16, [260, 1500, 9, 77], [130, 1, 1, 77]),             # group 8, d64
+    (16, 8, 128, 512, [1300, 1, 700, 3000, 513], [300, 1, 64, 1, 513]),  # blocks of 512
 ]
 
 
