@@ -210,10 +210,10 @@ static int32_t resolve_max_ctx(int32_t max_ctx, int32_t maxb, int32_t bs) {
 static int launch_merge(void* out, const DecodePlan& pl, const WsPtrs& w,
                         const int32_t* context_lens, int32_t B, int32_t HQ, int32_t D,
                         pa_dtype dtype, hipStream_t s) {
-  // Pieces per output row: at most one more than the slices per sequence (balanced), or
+  // Pieces per output row: about one more than the mean slices per sequence (balanced), or
   // the partitions of the longest sequence (fixed).
   const int64_t pieces = pl.mode == DecodePlan::kBalanced ? (pl.Wt + B - 1) / B + 1 : pl.NP;
-  const int W = merge_waves(pieces);
+  const int W = merge_waves(pieces, (int64_t)HQ * B);
   const dim3 grid(HQ, B), block(64 * W);
 #define PA_MERGE_W(ET, WV)                                                                       \
   if (pl.mode == DecodePlan::kBalanced)                                                          \
@@ -225,6 +225,10 @@ static int launch_merge(void* out, const DecodePlan& pl, const WsPtrs& w,
 #define PA_MERGE(ET)            \
   if (W == 1) {                 \
     PA_MERGE_W(ET, 1)           \
+  } else if (W == 2) {          \
+    PA_MERGE_W(ET, 2)           \
+  } else if (W == 4) {          \
+    PA_MERGE_W(ET, 4)           \
   } else {                      \
     PA_MERGE_W(ET, kMergeWaves) \
   }

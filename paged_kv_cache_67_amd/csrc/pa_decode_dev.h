@@ -526,19 +526,28 @@ __device__ __forceinline__ void decode_balanced_body(
 }
 
 
-// Merge workgroups: one wave, or kMergeWaves waves for rows with many pieces; each wave
-// keeps kMergeUnroll pieces' loads in flight.
+// Merge workgroups: 1, 2, 4 or kMergeWaves waves; each wave keeps up to kMergeUnroll pieces'
+// loads in flight.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeUnroll = 8;
-// Waves per merge workgroup for a given mean number of pieces per row.
-inline int merge_waves(int64_t pieces_per_row) { return pieces_per_row >= 16 ? kMergeWaves : 1; }
+// Waves per merge workgroup.  A grid of at most one workgroup per compute unit leaves most
+// of the chip idle, so the widest workgroup costs nothing there, and it is what a row far
+// longer than the rest (which the host cannot see) needs.  A larger grid pays for every
+// wave, so it gets the fewest waves whose loads in flight take a typical row's pieces
+// (pieces_per_row: the mean, or the most any row can have) in one round.
+inline int merge_waves(int64_t pieces_per_row, int64_t workgroups) {
+  if (workgroups <= kNumCUs) return kMergeWaves;
+  int w = 1;
+  while (w < kMergeWaves && (int64_t)w * kMergeUnroll < pieces_per_row) w *= 2;
+  return w;
+}
 
 // Combines n partial states (m, l, acc[D]) of one output row into out[row .. row + D):
 // out = sum_k e^(m_k - M) acc_k / sum_k e^(m_k - M) l_k with M = max_k m_k (m in natural-log
 // units, the rescaling identity of the online softmax).  Piece k's m and l sit at ws_m /
 // ws_l[idx(k)] and its acc at ws_acc[idx(k) * D].  Wave w takes pieces w, w + W, w + 2W, ...,
-// kMergeUnroll at a time with all their loads issued together (pieces past n read piece
-// n - 1 and count zero), keeping a running (M, L, A) that is rescaled when M grows; with
+// kMergeUnroll at a time with all their loads issued together (slots past n load nothing
+// and count zero), keeping a running (M, L, A) that is rescaled when M grows; with
 // W > 1 the wave states are combined through LDS.  Lane l holds d = l and, for D = 128,
 // d = l + 64.  Must be called by all 64 W threads of the workgroup.
 template <int ET, int W, typename Idx>
@@ -558,14 +567,15 @@ __device__ __forceinline__ void merge_states(void* __restrict__ out, int64_t row
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = k0 + w + W * u;
-      const bool ok = kk < n;
-      const int64_t s = idx(min(kk, n - 1));
-      const float mv = ws_m[s], lv = ws_l[s], av0 = ws_acc[s * D + lane];
-      const float av1 = two ? ws_acc[s * D + 64 + lane] : 0.0f;
-      m[u] = ok ? mv : kFloor;
-      l[u] = ok ? lv : 0.0f;
-      a0[u] = ok ? av0 : 0.0f;
-      a1[u] = ok ? av1 : 0.0f;
+      m[u] = kFloor;
+      l[u] = a0[u] = a1[u] = 0.0f;
+      if (kk < n) {  // wave-uniform
+        const int64_t s = idx(kk);
+        m[u] = ws_m[s];
+        l[u] = ws_l[s];
+        a0[u] = ws_acc[s * D + lane];
+        if (two) a1[u] = ws_acc[s * D + 64 + lane];
+      }
     }
     float mn = M;
 #pragma unroll

@@ -373,8 +373,9 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
                      head_waves, pl.Wt, (int)dec_wgs);
   int st = check_launch(fn);
   if (st) return st;
-  // Pieces per decode row: at most one more than the slices per sequence.
-  const int W = merge_waves((pl.Wt + num_seqs - 1) / num_seqs + 1);
+  // Pieces per decode row: about one more than the mean slices per sequence.
+  const int W = merge_waves((pl.Wt + num_seqs - 1) / num_seqs + 1,
+                            (int64_t)num_q_heads * num_seqs);
   const dim3 mgrid(num_q_heads, num_seqs);
 #define PA_MIXED_MERGE(ET, WV)                                                              \
   hipLaunchKernelGGL((merge_balanced_kernel<ET, true, WV>), mgrid, dim3(64 * WV), 0, s, out, \
@@ -382,9 +383,13 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
                      head_dim, pl.Wt)
   if (dtype == PA_F16) {
     if (W == 1) PA_MIXED_MERGE(PA_F16, 1);
+    else if (W == 2) PA_MIXED_MERGE(PA_F16, 2);
+    else if (W == 4) PA_MIXED_MERGE(PA_F16, 4);
     else PA_MIXED_MERGE(PA_F16, kMergeWaves);
   } else {
     if (W == 1) PA_MIXED_MERGE(PA_BF16, 1);
+    else if (W == 2) PA_MIXED_MERGE(PA_BF16, 2);
+    else if (W == 4) PA_MIXED_MERGE(PA_BF16, 4);
     else PA_MIXED_MERGE(PA_BF16, kMergeWaves);
   }
 #undef PA_MIXED_MERGE

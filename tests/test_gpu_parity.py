@@ -688,6 +688,42 @@ def test_decode_random_shapes(seed):
     assert_close(out_f64(out, c["dtype"]), want, c["dtype"], str(c))
 
 
+# Batches whose merge runs with each workgroup width (1, 2, 4 and 8 waves): a merge grid
+# (query heads x rows) of more than one workgroup per compute unit takes the fewest waves
+# that hold a typical row's pieces in one round, a smaller grid always 8.  Uniform lengths
+# with the first row at the maximum.
+MERGE_WIDTH_CASES = [
+    # waves, dtype, B, HQ, HKV, D, block_size, max context, partition_size
+    (1, "bf16", 300, 2, 2, 64, 16, 2500, 0),
+    (2, "bf16", 130, 4, 2, 64, 16, 2500, 0),
+    (2, "f16", 48, 8, 4, 64, 32, 1500, 0),
+    (4, "bf16", 90, 8, 1, 128, 16, 2500, 0),
+    (8, "bf16", 33, 16, 1, 128, 64, 2500, 0),
+    (1, "f32", 200, 4, 4, 128, 16, 600, 0),
+    (1, "bf16", 40, 8, 2, 64, 16, 2000, 512),
+    (2, "bf16", 200, 8, 2, 64, 16, 2000, 128),
+    (4, "f16", 40, 8, 2, 64, 16, 2000, 64),
+    (8, "bf16", 40, 8, 2, 64, 16, 2000, 16),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_WIDTH_CASES,
+                         ids=lambda c: f"w{c[0]}-{c[1]}-b{c[2]}-{c[3]}q{c[4]}kv-d{c[5]}-p{c[8]}")
+def test_decode_merge_widths(case):
+    """Every merge workgroup width, on the balanced split and on fixed partitions: every row
+    against the oracle."""
+    _, dtype, B, HQ, HKV, D, bs, max_ctx, P = case
+    r = np.random.default_rng(B * 31 + HQ)
+    lens = r.integers(1, max_ctx, size=B, endpoint=True).astype(np.int32)
+    lens[0] = max_ctx
+    w = make_workload(name="merge-width", kind="decode", dtype=dtype, num_q_heads=HQ,
+                      num_kv_heads=HKV, head_dim=D, block_size=bs, seq_lens_k=lens,
+                      seed=MERGE_WIDTH_CASES.index(case))
+    announce(f"decode merge width case {case}")
+    dw = run_hip(w, partition_size=P)
+    assert_close(out_f64(dw.out, dtype), OracleRun(w).decode(), dtype, str(case))
+
+
 @pytest.mark.parametrize("seed", list(range(20)))
 def test_store_random_tables(seed):
     """Seeded random varlen batches with holes in the block tables (-1 entries inside and
