@@ -161,34 +161,22 @@ __device__ __forceinline__ void prefill_body(
   const int qc = lane & 15, grp = lane >> 4;
   const int rg = w & 3;  // row group
   const int kh = w >> 2;  // key half
-  int64_t qtok[2];
-  bool rvalid[2];
-  int hq[2], row_nk[2];
+  int row_nk[2];
 #pragma unroll
   for (int qg = 0; qg < 2; ++qg) {
     const int row = 32 * rg + 16 * qg + qc;
     const int rpos = row / G;
-    qtok[qg] = (int64_t)q0 + pos0 + rpos;
-    rvalid[qg] = row < BM * G && rpos < npos && qtok[qg] >= 0 && qtok[qg] < total_q;
-    hq[qg] = g * G + row % G;
-    row_nk[qg] = (causal && rvalid[qg]) ? prefix + pos0 + rpos + 1 : nk;
+    const int64_t qtok = (int64_t)q0 + pos0 + rpos;
+    const bool rvalid = row < BM * G && rpos < npos && qtok >= 0 && qtok < total_q;
+    row_nk[qg] = (causal && rvalid) ? prefix + pos0 + rpos + 1 : nk;
   }
   const int nk_min = causal ? min(nk, prefix + pos0 + 1) : nk;
   const int bs_mask = (1 << bs_log2) - 1;
   const int HKVD = HKV * D;  // elements between consecutive tokens of a block
 
-  // B operand of S^T: this lane's queries, d = 32ds + 8*grp + 0..7.  A row past the
-  // sequence reads a clamped (valid) token instead: rows never mix and such a row is not
-  // stored, and unconditional loads keep the compiler from draining the queue after each.
+  // B operand of S^T: this lane's queries, d = 32ds + 8*grp + 0..7 (read from the query
+  // tile staged in LDS before the first scores).
   v8 qreg[2][DS];
-#pragma unroll
-  for (int qg = 0; qg < 2; ++qg) {
-    const int64_t tok = min(max(qtok[qg], (int64_t)0), (int64_t)total_q - 1);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qreg[qg][ds] = __builtin_bit_cast(
-          v8, *reinterpret_cast<const uint4*>(q + (tok * HQ + hq[qg]) * D + 32 * ds + 8 * grp));
-  }
 
   // s_bt[i] holds block-table entry btb + i for i < nv = min(nblk - btb, kBtCache), each
   // checked against the pool when loaded (a bad id marks the output and reads block 0).
@@ -351,12 +339,13 @@ __device__ __forceinline__ void prefill_body(
   auto step = [&](int t) __attribute__((always_inline)) {
     const int kt = t * BN;
     // V_{t+1} and K_{t+2} into the buffers step t - 1 finished reading.
+    // (None past the last tile: the last steps' waits then cover no dead loads.)
     if constexpr (WIDE) {
-      issue_at(next_v, sKV[2 + ((t + 1) & 1)]);
-      issue_at(next_k, sKV[t & 1]);
+      if (t + 1 < ntiles) issue_at(next_v, sKV[2 + ((t + 1) & 1)]);
+      if (t + 2 < ntiles) issue_at(next_k, sKV[t & 1]);
     } else {
-      issue_v(t + 1);
-      issue_k(t + 2);
+      if (t + 1 < ntiles) issue_v(t + 1);
+      if (t + 2 < ntiles) issue_k(t + 2);
     }
     if (kt + BN > nk_min) {
 #pragma unroll
@@ -480,23 +469,44 @@ __device__ __forceinline__ void prefill_body(
   };
 
   if (ntiles > 0) {
+    // The query tile goes through LDS (the last V buffer, free until step 0) like a K tile,
+    // so that the first scores wait only for Q and K_0 while V_0 and K_1 land (Q in
+    // registers would have the compiler wait for every load, as it does not count the
+    // tile loads).  Rows past the sequence read a clamped (valid) token: rows never mix
+    // and such a row is not stored.
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int rpos = trow[i] / G;
+      const int64_t tok = min(max((int64_t)q0 + pos0 + rpos, (int64_t)0), (int64_t)total_q - 1);
+      load_to_lds(q + (tok * HQ + g * G + trow[i] % G) * D + (tcol[i] - g * D),
+                  (uint32_t)(uintptr_t)(sKV[3] + 512 * (wu + 8 * i)));
+    }
     issue_k(0);
     issue_v(0);
-    issue_k(1);
+    if (ntiles > 1) issue_k(1);
     if constexpr (WIDE) {
       next_v = locate(vc, BN);
       cover(2 * BN);
       next_k = locate(kc, 2 * BN);
     }
-    // Settle the Q loads here: the compiler does not count the tile loads, so this wait
-    // also covers K_0, V_0 and K_1.
+    // Loads complete in issue order: with V_0 and K_1 (LPT each) still allowed in flight,
+    // this wave's parts of Q and K_0 have landed; the barrier publishes everyone's.
+    asm volatile("" ::: "memory");
+    if (ntiles > 1)
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (2 * LPT));  // vmcnt(2 LPT) expcnt(7) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt((7 << 4) | LPT);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg)
+    for (int qg = 0; qg < 2; ++qg) {
+      const int r = 32 * rg + 16 * qg + qc;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) asm volatile("" : "+v"(qreg[qg][ds]));
-    bar_tiles();
+      for (int ds = 0; ds < DS; ++ds)
+        qreg[qg][ds] = *reinterpret_cast<const v8*>(&sKV[3][r * D + (((4 * ds + grp) ^ swz(r)) * 8)]);
+    }
     scores(sKV[0], sc);
-    bar_tiles();  // step 0 refills buffer 0
+    bar_tiles();  // V_0, K_1 landed; Q read, so step 0 may refill buffers 0 and 3
     for (int t = 0; t < ntiles; ++t) step(t);
   }
 
