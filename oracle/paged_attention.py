@@ -76,7 +76,9 @@ def slot_mapping(block_table, cu_seqlens_q, seq_lens_k, block_size) -> np.ndarra
 
     A position whose logical block has no physical block (index past the table
     or a -1 entry) gets slot -1, the pages' "do not write" marker
-    ([MinivLLM] store_kvcache).
+    ([MinivLLM] store_kvcache).  So does a negative position (a sequence with
+    fewer keys than new tokens, e.g. a decode row of context length 0): it has
+    no logical block at all.
     """
     bt = np.asarray(block_table)
     cu = np.asarray(cu_seqlens_q)
@@ -87,7 +89,7 @@ def slot_mapping(block_table, cu_seqlens_q, seq_lens_k, block_size) -> np.ndarra
         for i in range(lq):
             p = int(lens[b]) - lq + i
             j = p // block_size
-            blk = int(bt[b, j]) if j < bt.shape[1] else -1
+            blk = int(bt[b, j]) if 0 <= j < bt.shape[1] else -1
             out[int(cu[b]) + i] = blk * block_size + p % block_size if blk >= 0 else -1
     return out
 

@@ -126,6 +126,15 @@ def check_slot_decode_log(ns):
     assert s.tolist() == g["slot_mapping"], s
 
 
+def check_slot_no_position(ns):
+    """A new token at a negative position has no logical block ([KVblog] 3.1: slots exist for
+    positions 0 .. len - 1 of a sequence): slot -1, whatever the table's last entry holds."""
+    bt = np.array([[5, 9], [3, -1]], dtype=np.int32)
+    # a decode row of context 0, then a row with 3 new tokens but only 2 keys
+    s = ns.slot_mapping(bt, np.array([0, 1, 4]), np.array([0, 2]), 16)
+    assert s.tolist() == [-1, -1, 48, 49], s
+
+
 def check_positions(ns):
     """Positions of new tokens (slot = position under an identity block table)."""
     sx = golden("slot_examples.json")
@@ -402,7 +411,7 @@ def check_prefix_split(ns):
 
 ALL_CHECKS = [
     check_slot_teaching, check_slot_boundaries, check_slot_prefill_log, check_slot_decode_log,
-    check_positions, check_store, check_softmax_example, check_hand_example,
+    check_slot_no_position, check_positions, check_store, check_softmax_example, check_hand_example,
     check_cached_append, check_decode_vs_sdpa, check_block_permutation, check_single_key,
     check_gqa_is_repeat, check_empty_context, check_partials_merge, check_causal_matrix,
     check_future_change, check_prefill_vs_sdpa, check_prefix_split,

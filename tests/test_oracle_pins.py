@@ -42,6 +42,7 @@ MUTANTS = [
     ("bf16 widening shift", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("copy_blocks copies K only", "        v_pool[dst] = v_pool[src]\n", "\n"),
     ("copy_blocks direction swapped", "k_pool[dst] = k_pool[src]", "k_pool[src] = k_pool[dst]"),
+    ("negative positions wrap to the table's end", "if 0 <= j < bt.shape[1] else -1", "if j < bt.shape[1] else -1"),
     ("copy_blocks keeps out-of-range pairs", "if not (0 <= src < nb and 0 <= dst < nb) or src == dst:", "if src == dst:"),
 ]
 
