@@ -182,7 +182,8 @@ def time_prefill(args):
 
 
 def time_other_decode(args):
-    """pa_decode (both passes) on the two other decode workloads: Qwen2.5-0.5B shape
+    """pa_decode (both passes), and the whole step (store + decode as two calls and as one
+    pa_decode_append), on the two other decode workloads: Qwen2.5-0.5B shape
     (batch 64, 14 Q / 2 KV heads, d64, block 16) and the skewed long-context batch (one
     32768-token sequence and seven of 512).  Each fits in the 256 MB Infinity Cache, so
     the launches rotate over enough buffer sets (own pools) to touch about 1 GB, one
@@ -212,15 +213,31 @@ def time_other_decode(args):
             for dw in sets:
                 dw.attention()
 
-        us = _graph_us(all_sets, max(10, args.steps // 10)) / nsets
+        def two_calls():
+            for dw in sets:
+                dw.store_paged(write_slots=False)
+                dw.attention()
+
+        def one_call():
+            for dw in sets:
+                dw.attention_append()
+
+        reps = max(10, args.steps // 10)
+        us = _graph_us(all_sets, reps) / nsets
+        us_two = _graph_us(two_calls, reps) / nsets
+        us_one = _graph_us(one_call, reps) / nsets
         gbs = nbytes / (us * 1e-6) / 1e9
-        log(f"{w.name}: pa_decode {us:.1f} us, {gbs:.1f} GB/s over {nsets} buffer sets")
+        log(f"{w.name}: pa_decode {us:.1f} us, {gbs:.1f} GB/s over {nsets} buffer sets; "
+            f"step (store + decode) {us_two:.1f} us as two calls, {us_one:.1f} us as "
+            f"pa_decode_append")
         res[w.name] = {"us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
                        "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                       "buffer_sets": nsets}
+                       "buffer_sets": nsets, "us_step_store_then_decode": round(us_two, 2),
+                       "us_step_decode_append": round(us_one, 2)}
         del sets
         torch.cuda.empty_cache()
-    res["timing"] = "HIP graph of one pa_decode per buffer set, replayed between two events"
+    res["timing"] = ("HIP graph of one pa_decode per buffer set, replayed between two events; "
+                     "the steps: pa_store_kv_paged + pa_decode, and pa_decode_append")
     return res
 
 
@@ -248,8 +265,9 @@ def _graph_us(fn, reps, rounds=5):
 
 
 def time_graphs(w, dw, args):
-    """Decode steps (slot addressing + scatter + decode + merge) for the first n sequences
-    of the decode batch: launched eagerly from Python against replayed from the HIP graph
+    """Decode steps (slot addressing + store + decode + merge: one pa_decode_append call) for
+    the first n sequences of the decode batch: launched eagerly from Python against replayed
+    from the HIP graph
     of their batch bucket, with the inputs staged into the graph's fixed buffers each step
     (one pa_copy_many launch) and with them already in place (bare replay)."""
     import torch

@@ -267,6 +267,54 @@ int pa_decode_merge(void* out, const void* workspace, const int32_t* context_len
                     int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                     pa_dtype dtype, void* stream);
 
+/*
+ * pa_decode_append -- a decode step's store and attention in one call:
+ * pa_store_kv_paged of the step's new rows (one per sequence, row b at key
+ * context_lens[b] - 1 of sequence b) followed by pa_decode, with the same
+ * results ([MinivLLM] Attention.forward: the new K/V go to the cache, then the
+ * query attends over every key including its own; [mini] section 5 for the
+ * decode).  With the balanced split the store is part of the first pass: the
+ * wave that finishes a sequence takes its last key from the new rows instead
+ * of the cache and writes them to their slot, so the step needs no store
+ * launch.  With another plan (single pass, fixed partitions) the rows are
+ * stored by a launch of their own first.
+ *
+ *   key, value   in  [num_seqs][num_kv_heads][head_dim] rows of the step's new
+ *                    token, token strides key_token_stride / value_token_stride
+ *                    in elements (>= num_kv_heads * head_dim; 16-byte aligned
+ *                    rows); dtype as the cache
+ *   k_cache, v_cache  in/out: the pool; it holds the first context_lens[b] - 1
+ *                    keys of sequence b before the call and all of them after
+ *   everything else  as for pa_decode (context_lens counts the new key)
+ *
+ * A sequence with context_lens[b] = 0 has no new row (nothing is stored; zero
+ * output row).  The new rows' slots must be distinct, and no other sequence
+ * may read them.  Errors as for pa_decode and pa_store_kv_paged.
+ */
+int pa_decode_append(void* out, const void* q, const void* key, const void* value,
+                     int64_t key_token_stride, int64_t value_token_stride, void* k_cache,
+                     void* v_cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                     int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, float scale, pa_dtype dtype,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * pa_decode_append_partitions -- the first pass of pa_decode_append on its own
+ * (with the store), as pa_decode_partitions is pa_decode's:
+ * pa_decode_append = pa_decode_append_partitions + pa_decode_merge.
+ */
+int pa_decode_append_partitions(void* out, const void* q, const void* key, const void* value,
+                                int64_t key_token_stride, int64_t value_token_stride,
+                                void* k_cache, void* v_cache, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, int32_t num_blocks,
+                                int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, float scale, pa_dtype dtype,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Bytes of the scratch array inside the library that pa_decode_noalloc uses (per device). */
 #define PA_NOALLOC_SCRATCH_BYTES (16 << 20)
 
@@ -458,8 +506,10 @@ int pa_read_ceiling(const void* k_cache, const void* v_cache, const int32_t* blo
  * for debugging and tests, not for the hot path (it synchronises, so it
  * cannot be captured in a graph).  When the checks are switched on, the
  * matching check runs at the start of pa_store_kv, pa_store_kv_paged,
- * pa_decode, pa_decode_partitions, pa_prefill_paged and pa_attention_mixed,
- * which then return its status instead of launching.  They start switched on
+ * pa_decode, pa_decode_partitions, pa_decode_append(_partitions),
+ * pa_prefill_paged and pa_attention_mixed, which then return its status
+ * instead of launching (pa_decode_append: the decode check, then no two new
+ * rows in one slot).  They start switched on
  * when the environment variable PA_DEBUG_CHECKS is set to anything but "0" at
  * the first call that looks; pa_set_debug_checks(on) switches them for the
  * whole process and returns the previous setting (0 / 1).

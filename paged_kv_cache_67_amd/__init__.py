@@ -25,6 +25,8 @@ from ._binding import (  # noqa: F401
     pa_copy_many,
     pa_read_ceiling,
     pa_decode,
+    pa_decode_append,
+    pa_decode_append_partitions,
     pa_decode_merge,
     pa_decode_noalloc,
     pa_decode_partitions,

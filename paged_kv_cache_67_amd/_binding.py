@@ -47,6 +47,12 @@ SIGNATURES = {
                             _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
     "pa_decode_partitions": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _f32, C.c_int, _i32, _vp, _sz, _vp]),
+    "pa_decode_append": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _i32,
+                                   _i32, _i32, _i32, _i32, _i32, _i32, _f32, C.c_int, _i32, _vp,
+                                   _sz, _vp]),
+    "pa_decode_append_partitions": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32,
+                                              _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                              C.c_int, _i32, _vp, _sz, _vp]),
     "pa_decode_merge": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pa_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _f32, C.c_int, _i32, _vp]),
@@ -250,6 +256,43 @@ def pa_decode_partitions(out, q, k_cache, v_cache, block_table, context_lens, sc
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(context_lens), B, int(max_context_len), NB, BS, HQ, HKV, D, float(scale), _dtype(q),
         int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _decode_append(name, out, q, key, value, k_cache, v_cache, block_table, context_lens, scale,
+                   max_context_len, partition_size, workspace, stream):
+    B, HQ, D = q.shape
+    NB, BS, HKV, Dk = k_cache.shape
+    assert Dk == D and v_cache.shape == k_cache.shape and q.dtype == k_cache.dtype == v_cache.dtype
+    assert q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()
+    for t in (key, value):
+        assert t.dim() == 3 and t.shape == (B, HKV, D) and t.stride(2) == 1 and t.stride(1) == D
+        assert t.dtype == k_cache.dtype
+    if out is not None:
+        assert out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous()
+    assert block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.shape[0] == B
+    _i32_vec(context_lens, B, "context_lens")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(name, getattr(lib(), name)(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(context_lens), B,
+        int(max_context_len), NB, BS, HQ, HKV, D, float(scale), _dtype(q), int(partition_size),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_append(out, q, key, value, k_cache, v_cache, block_table, context_lens, scale,
+                     max_context_len=0, partition_size=0, workspace=None, stream=None):
+    """The step's new rows key / value [B, HKV, D] (row b: key context_lens[b] - 1 of sequence
+    b) stored to the cache, then pa_decode over every key; one first pass with the balanced
+    split."""
+    _decode_append("pa_decode_append", out, q, key, value, k_cache, v_cache, block_table,
+                   context_lens, scale, max_context_len, partition_size, workspace, stream)
+
+
+def pa_decode_append_partitions(out, q, key, value, k_cache, v_cache, block_table, context_lens,
+                                scale, max_context_len, partition_size, workspace, stream=None):
+    _decode_append("pa_decode_append_partitions", out, q, key, value, k_cache, v_cache,
+                   block_table, context_lens, scale, max_context_len, partition_size, workspace,
+                   stream)
 
 
 def pa_decode_merge(out, workspace, context_lens, num_kv_heads, max_context_len, partition_size,

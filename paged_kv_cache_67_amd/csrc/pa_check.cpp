@@ -4,8 +4,8 @@
 // the first broken rule of a batch, for debugging and tests.  With the checks switched on
 // (PA_DEBUG_CHECKS set to anything but "0" in the environment when the library first looks,
 // or pa_set_debug_checks(1)), pa_store_kv, pa_store_kv_paged, pa_decode, pa_decode_partitions,
-// pa_prefill_paged and pa_attention_mixed run them before every launch, which synchronises
-// the stream and so cannot be captured in a graph.
+// pa_decode_append(_partitions), pa_prefill_paged and pa_attention_mixed run them before every
+// launch, which synchronises the stream and so cannot be captured in a graph.
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -57,6 +57,26 @@ static int check_rows(const std::vector<int32_t>& bt, int32_t maxb, int32_t b, i
     if (v < 0 || v >= num_blocks)
       return fail(PA_ERR_CONTRACT, "%s: block_table[%d][%lld] = %d outside [0, %d)", what, b,
                   (long long)i, v, num_blocks);
+  }
+  return PA_OK;
+}
+
+int check_append_slots(const int32_t* block_table, int32_t maxb, const int32_t* context_lens,
+                       int32_t B, int32_t num_blocks, int32_t block_size, hipStream_t s) {
+  const char* what = "pa_decode_append";
+  std::vector<int32_t> ctx, bt;
+  if (int st = fetch(ctx, context_lens, B, s, what)) return st;
+  if (int st = fetch(bt, block_table, (int64_t)B * maxb, s, what)) return st;
+  std::unordered_set<int64_t> seen;
+  for (int32_t b = 0; b < B; ++b) {
+    if (ctx[b] <= 0) continue;
+    const int64_t p = (int64_t)ctx[b] - 1;
+    if (p / block_size >= maxb) continue;  // pa_check_decode_inputs names it
+    const int32_t blk = bt[(size_t)b * maxb + p / block_size];
+    if (blk < 0 || blk >= num_blocks) continue;  // pa_check_decode_inputs names it
+    if (!seen.insert((int64_t)blk * block_size + p % block_size).second)
+      return fail(PA_ERR_CONTRACT, "%s: the new rows of two sequences share slot %lld (sequence %d)",
+                  what, (long long)((int64_t)blk * block_size + p % block_size), b);
   }
   return PA_OK;
 }

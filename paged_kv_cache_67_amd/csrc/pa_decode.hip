@@ -111,19 +111,22 @@ __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_kernel(
 // hold max_head_waves(G) waves whatever the number of head waves, so that the grid is
 // about one workgroup per compute unit and every unit runs the same number of waves
 // (with one workgroup per slice, 4 head waves made 4-wave workgroups, 1.5 per unit).
-template <int D, int ET, int G>
+// APPEND: the cache holds the first context_lens[b] - 1 keys of each sequence and the last
+// comes from the step's new rows `ap`, which the launch also stores to their slots.
+template <int D, int ET, int G, bool APPEND>
 __global__ __launch_bounds__(max_head_waves(G) * 64) void decode_balanced_kernel(
     void* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_m,
     float* __restrict__ ws_l, int32_t* __restrict__ ws_cuc, const void* __restrict__ qptr,
     const void* __restrict__ kcache, const void* __restrict__ vcache,
     const int32_t* __restrict__ block_table, int maxb, const int32_t* __restrict__ context_lens,
-    int B, int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt) {
+    int B, int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt,
+    AppendRows ap) {
   const int head_waves = HKV * (group / G);
   const int item = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  decode_balanced_body<D, ET, G, false>(
+  decode_balanced_body<D, ET, G, false, APPEND>(
       item / head_waves, item % head_waves, blockIdx.x == 0, out, ws_acc, ws_m, ws_l, ws_cuc,
       qptr, kcache, vcache, block_table, maxb, context_lens, nullptr, nullptr, 0, B, num_blocks,
-      bs_log2, HQ, HKV, group, scale_log2, Wt);
+      bs_log2, HQ, HKV, group, scale_log2, Wt, ap);
 }
 
 // ---------------------------------------------------------------------------
@@ -155,27 +158,38 @@ typedef void (*decode_fn)(void*, float*, float*, float*, const void*, const void
                           int, int);
 typedef void (*balanced_fn)(void*, float*, float*, float*, int32_t*, const void*, const void*,
                             const void*, const int32_t*, int, const int32_t*, int, int, int, int,
-                            int, int, float, int);
+                            int, int, float, int, AppendRows);
+
+// The appending first pass keeps two waves per SIMD without spills for every head tile in
+// bf16 and fp32, and in fp16 for tiles of 1, 2, 3 and 5 query heads (4 and 6 spill, 7 and 8
+// fit only one wave per SIMD); those fp16 tiles store the new rows with a launch of their own.
+template <int D, int ET, int G>
+static balanced_fn append_kernel() {
+  if constexpr (ET != PA_F16 || G <= 3 || G == 5) return decode_balanced_kernel<D, ET, G, true>;
+  else return nullptr;
+}
 
 template <int D, int ET>
-static void pick_g(int G, decode_fn* f, balanced_fn* fb) {
+static void pick_g(int G, decode_fn* f, balanced_fn* fb, balanced_fn* fa) {
   switch (G) {
-#define PA_CASE(g)                          \
-  case g:                                   \
-    *f = decode_kernel<D, ET, g>;           \
-    *fb = decode_balanced_kernel<D, ET, g>; \
+#define PA_CASE(g)                                \
+  case g:                                         \
+    *f = decode_kernel<D, ET, g>;                 \
+    *fb = decode_balanced_kernel<D, ET, g, false>; \
+    *fa = append_kernel<D, ET, g>();               \
     return;
     PA_CASE(1) PA_CASE(2) PA_CASE(3) PA_CASE(4) PA_CASE(5) PA_CASE(6) PA_CASE(7) PA_CASE(8)
 #undef PA_CASE
   }
   *f = nullptr;
   *fb = nullptr;
+  *fa = nullptr;
 }
 
-static void pick_decode(int D, pa_dtype dt, int G, decode_fn* f, balanced_fn* fb) {
-  if (dt == PA_BF16) D == 64 ? pick_g<64, PA_BF16>(G, f, fb) : pick_g<128, PA_BF16>(G, f, fb);
-  else if (dt == PA_F16) D == 64 ? pick_g<64, PA_F16>(G, f, fb) : pick_g<128, PA_F16>(G, f, fb);
-  else D == 64 ? pick_g<64, PA_F32>(G, f, fb) : pick_g<128, PA_F32>(G, f, fb);
+static void pick_decode(int D, pa_dtype dt, int G, decode_fn* f, balanced_fn* fb, balanced_fn* fa) {
+  if (dt == PA_BF16) D == 64 ? pick_g<64, PA_BF16>(G, f, fb, fa) : pick_g<128, PA_BF16>(G, f, fb, fa);
+  else if (dt == PA_F16) D == 64 ? pick_g<64, PA_F16>(G, f, fb, fa) : pick_g<128, PA_F16>(G, f, fb, fa);
+  else D == 64 ? pick_g<64, PA_F32>(G, f, fb, fa) : pick_g<128, PA_F32>(G, f, fb, fa);
 }
 
 static int validate_common(const char* fn, int32_t num_seqs, int32_t num_q_heads,
@@ -249,13 +263,24 @@ static int launch_decode(const char* fn, const DecodePlan& pl, void* out, const 
                          const void* k_cache, const void* v_cache, const int32_t* block_table,
                          int32_t maxb, const int32_t* context_lens, int32_t B, int32_t NB,
                          int32_t bs, int32_t HQ, int32_t HKV, int32_t D, float scale,
-                         pa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t s) {
+                         pa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t s,
+                         const AppendRows* ap = nullptr, bool fuse = true) {
   if (pl.mode != DecodePlan::kSingle && (!workspace || workspace_bytes < pl.ws_bytes))
     return fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
                 pl.ws_bytes);
   decode_fn kern;
-  balanced_fn bkern;
-  pick_decode(D, dtype, pl.G, &kern, &bkern);
+  balanced_fn bkern, akern;
+  pick_decode(D, dtype, pl.G, &kern, &bkern, &akern);
+  // The appending first pass exists for the balanced split (and the tiles append_kernel
+  // names) and is used when the caller asks for it (fuse); otherwise the new rows are stored
+  // by a launch of their own first and the first pass reads them from the cache.
+  if (ap && (pl.mode != DecodePlan::kBalanced || !akern || !fuse)) {
+    if (int st = launch_store_decode_rows(ap->key, ap->value, ap->key_stride, ap->value_stride,
+                                          ap->kc, ap->vc, block_table, maxb, context_lens, B, NB,
+                                          bs, (int64_t)HKV * D * elt_bytes(dtype), s))
+      return st;
+    ap = nullptr;
+  }
   if (!kern) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for head tile %d", fn, pl.G);
   const int group = HQ / HKV;
   const int head_waves = HKV * (group / pl.G);
@@ -267,9 +292,10 @@ static int launch_decode(const char* fn, const DecodePlan& pl, void* out, const 
     const int wpg = max_head_waves(pl.G);
     const int64_t n_wg = ceil_div((int64_t)pl.Wt * head_waves, wpg);
     if (n_wg > INT32_MAX) return fail(PA_ERR_SHAPE, "%s: grid too large", fn);
-    hipLaunchKernelGGL(bkern, dim3((unsigned)n_wg), dim3(wpg * 64), lds, s, out, w.acc, w.m, w.l,
-                       w.cuc, q, k_cache, v_cache, block_table, maxb, context_lens, B, NB,
-                       __builtin_ctz(bs), HQ, HKV, group, scale * kLog2e, pl.Wt);
+    hipLaunchKernelGGL(ap ? akern : bkern, dim3((unsigned)n_wg), dim3(wpg * 64), lds, s, out,
+                       w.acc, w.m, w.l, w.cuc, q, k_cache, v_cache, block_table, maxb,
+                       context_lens, B, NB, __builtin_ctz(bs), HQ, HKV, group, scale * kLog2e,
+                       pl.Wt, ap ? *ap : AppendRows{});
   } else {
     const bool split = pl.mode == DecodePlan::kFixed;
     hipLaunchKernelGGL(kern, dim3(split ? pl.NP : 1, groups, B), dim3(wpb * 64), 0, s, out, w.acc,
@@ -408,6 +434,97 @@ extern "C" int pa_decode_merge(void* out, const void* workspace, const int32_t* 
   }
   return launch_merge(out, pl, carve(const_cast<void*>(workspace), pl, num_seqs, num_q_heads, head_dim),
                       context_lens, num_seqs, num_q_heads, head_dim, dtype, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// pa_decode_append(_partitions): the store of the step's new K/V rows and the decode in one
+// first pass (balanced split), or the store's own launch before it (other plans).
+
+namespace pa {
+
+static int decode_append(const char* fn, bool merge, void* out, const void* q, const void* key,
+                         const void* value, int64_t key_token_stride, int64_t value_token_stride,
+                         void* k_cache, void* v_cache, const int32_t* block_table, int32_t maxb,
+                         const int32_t* context_lens, int32_t B, int32_t max_ctx, int32_t NB,
+                         int32_t bs, int32_t HQ, int32_t HKV, int32_t D, float scale,
+                         pa_dtype dtype, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = validate_decode(fn, q, k_cache, v_cache, block_table, maxb, context_lens, B, NB, bs,
+                           HQ, HKV, D, dtype, workspace);
+  if (st || B == 0) return st;
+  if ((st = validate_partition(fn, partition_size))) return st;
+  if (!key || !value) return fail(PA_ERR_NULL, "%s: null new rows", fn);
+  if (key_token_stride < (int64_t)HKV * D || value_token_stride < (int64_t)HKV * D)
+    return fail(PA_ERR_SHAPE, "%s: token stride smaller than a row", fn);
+  const int eb = elt_bytes(dtype);
+  if (!aligned16(key) || !aligned16(value) || (key_token_stride * eb) % 16 ||
+      (value_token_stride * eb) % 16)
+    return fail(PA_ERR_ALIGN, "%s: new rows and their strides must be 16-byte aligned", fn);
+  if ((int64_t)NB * bs > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "%s: num_blocks*block_size exceeds int32 slots", fn);
+  max_ctx = resolve_max_ctx(max_ctx, maxb, bs);
+  if (!merge && (partition_size == -1 || !workspace))
+    return fail(PA_ERR_WORKSPACE, "%s: a split needs a workspace", fn);
+  if (debug_checks() &&
+      ((st = pa_check_decode_inputs(block_table, maxb, context_lens, B, max_ctx, NB, bs, stream)) ||
+       (st = check_append_slots(block_table, maxb, context_lens, B, NB, bs, (hipStream_t)stream))))
+    return st;
+  const DecodePlan pl = plan_decode(B, HQ, HKV, D, dtype, max_ctx, partition_size,
+                                    !merge || workspace != nullptr);
+  if (!merge && pl.mode == DecodePlan::kSingle)
+    return fail(PA_ERR_UNSUPPORTED, "%s: partition_size %d does not split max_context_len %d", fn,
+                partition_size, max_ctx);
+  if ((merge || pl.mode == DecodePlan::kBalanced) && (!out || !aligned16(out)))
+    return fail(out ? PA_ERR_ALIGN : PA_ERR_NULL, "%s: out must be a 16-byte aligned pointer", fn);
+  const AppendRows ap{static_cast<const char*>(key), static_cast<const char*>(value),
+                      key_token_stride * eb, value_token_stride * eb,
+                      static_cast<char*>(k_cache), static_cast<char*>(v_cache)};
+  // The store goes into the first pass when slices are short: the appending pass costs
+  // ~0.05 us more per chunk of a slice, so a batch whose slices are long (the 256-row
+  // Qwen3-0.6B decode: 182 chunks, 8.5 us more) is faster with the store's own ~4.6 us
+  // launch.  The slice length is bounded as if every sequence held max_ctx keys.
+  constexpr int64_t kAppendChunks = 128;
+  const int64_t ch = chunk_tokens(D, eb, pl.G);
+  const bool fuse = pl.mode == DecodePlan::kBalanced &&
+                    ceil_div((int64_t)B * ceil_div(max_ctx, ch), pl.Wt) <= kAppendChunks;
+  const hipStream_t s = (hipStream_t)stream;
+  st = launch_decode(fn, pl, out, q, k_cache, v_cache, block_table, maxb, context_lens, B, NB, bs,
+                     HQ, HKV, D, scale, dtype, workspace, workspace_bytes, s, &ap, fuse);
+  if (st || !merge || pl.mode == DecodePlan::kSingle) return st;
+  return launch_merge(out, pl, carve(workspace, pl, B, HQ, D), context_lens, B, HQ, D, dtype, s);
+}
+
+}  // namespace pa
+
+extern "C" int pa_decode_append(void* out, const void* q, const void* key, const void* value,
+                                int64_t key_token_stride, int64_t value_token_stride,
+                                void* k_cache, void* v_cache, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, int32_t num_blocks,
+                                int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, float scale, pa_dtype dtype,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_append("pa_decode_append", true, out, q, key, value, key_token_stride,
+                       value_token_stride, k_cache, v_cache, block_table, max_blocks_per_seq,
+                       context_lens, num_seqs, max_context_len, num_blocks, block_size,
+                       num_q_heads, num_kv_heads, head_dim, scale, dtype, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_append_partitions(
+    void* out, const void* q, const void* key, const void* value, int64_t key_token_stride,
+    int64_t value_token_stride, void* k_cache, void* v_cache, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+    int32_t max_context_len, int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, float scale, pa_dtype dtype, int32_t partition_size,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_append("pa_decode_append_partitions", false, out, q, key, value,
+                       key_token_stride, value_token_stride, k_cache, v_cache, block_table,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_blocks,
+                       block_size, num_q_heads, num_kv_heads, head_dim, scale, dtype,
+                       partition_size, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

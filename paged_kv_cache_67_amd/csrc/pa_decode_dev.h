@@ -127,6 +127,17 @@ constexpr int kHeadSlot = 0;  // partial state of a piece whose sequence began b
 constexpr int kTailSlot = 1;  // partial state of a piece whose sequence runs past the slice
 constexpr int kMaxBalancedSeqs = 8192;  // LDS holds 2 ints per sequence
 
+// The step's new K/V rows of a decode launch that also appends them to the cache: one row
+// per sequence, laid out like a cache row (all KV heads), row b at key / value + b * stride
+// bytes; kc / vc are the caches they go to.
+struct AppendRows {
+  const char* key;
+  const char* value;
+  int64_t key_stride, value_stride;
+  char* kc;
+  char* vc;
+};
+
 template <int U>
 struct KVRegs {
   uint4 k[U], v[U];
@@ -317,6 +328,41 @@ struct DecodeWave {
       }
     }
   }
+
+  // issue() where key `fresh_t` (end - 1 in a sequence's last chunk, else -1) is the step's
+  // new row: every lane whose (clamped) token is fresh_t loads it from nk / nv (the row's
+  // first byte) instead of the cache, so the chunk is computed as if the row had been stored
+  // first and no lane reads the slot it goes to.  One load path for every chunk: a branch
+  // between two would leave the compiler's load counting conservative where they join.
+  __device__ __forceinline__ void issue_last(KVRegs<U>& X, int t0, int end, const int* ids,
+                                             int fresh_t, const char* nk, const char* nv) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(t0 + u * RG + r, end - 1);
+      const bool ok = ids[u] >= 0 && ids[u] < num_blocks;
+      bad |= !ok;
+      const int64_t base = (int64_t)(ok ? ids[u] : 0) * blk_bytes;
+      const uint32_t off = (uint32_t)(t & bs_mask) * row_bytes + lane_off;
+      const bool fresh = t == fresh_t;
+      X.k[u] = load_stream16(fresh ? nk + lane_off : kc + base + off);
+      X.v[u] = load_stream16(fresh ? nv + lane_off : vc + base + off);
+    }
+  }
+
+  // After the chunk issued by issue_last has been computed: the lanes that hold key end - 1
+  // (unclamped) write it to its slot in block `blk` (one 16-byte piece each).  A block id out
+  // of range writes nothing; the chunk's loads have already poisoned the row.
+  __device__ __forceinline__ void store_new(const KVRegs<U>& X, int t0, int end, int blk,
+                                            char* kcw, char* vcw) const {
+    if (blk < 0 || blk >= num_blocks) return;
+    const int64_t off = (int64_t)blk * blk_bytes + (int64_t)((end - 1) & bs_mask) * row_bytes + lane_off;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + u * RG + r == end - 1) {
+        *reinterpret_cast<uint4*>(kcw + off) = X.k[u];
+        *reinterpret_cast<uint4*>(vcw + off) = X.v[u];
+      }
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -410,13 +456,14 @@ __device__ __forceinline__ int balanced_scan(int* s_mem, const int32_t* __restri
 // barrier: slice w of head wave hw (a KV head and a G-wide tile of its query heads), over
 // the tables at s_mem.  write_cuc: this workgroup also leaves s_cuc in the workspace for
 // the merge.
-template <int D, int ET, int G, bool VARLEN>
+template <int D, int ET, int G, bool VARLEN, bool APPEND = false>
 __device__ __forceinline__ void decode_balanced_run(
     const int* s_mem, int w, int hw, bool write_cuc, void* __restrict__ out,
     float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
     int32_t* __restrict__ ws_cuc, const void* __restrict__ qptr, const void* __restrict__ kcache,
     const void* __restrict__ vcache, const int32_t* __restrict__ block_table, int maxb, int B,
-    int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt) {
+    int num_blocks, int bs_log2, int HQ, int HKV, int group, float scale_log2, int Wt,
+    const AppendRows& ap = AppendRows{}) {
   using W = DecodeWave<D, ET, G>;
   constexpr int CH = W::CH;
   constexpr int U = W::U;
@@ -455,10 +502,25 @@ __device__ __forceinline__ void decode_balanced_run(
   st.load_q(qptr, (int64_t)c0.row * HQ + h0);
 
   auto bt_of = [&](const Cursor& c) { return block_table + (int64_t)c.b * maxb; };
-  // After the chunk at c: if it closes a piece (its sequence's last chunk or the
+  // APPEND: the cache holds keys [0, L - 1) of each sequence and key L - 1 is the step's new
+  // row, which the sequence's last chunk loads from the new rows (issue_last) and one head
+  // wave per KV head then stores to its slot (store_new).
+  auto iss = [&](KVRegs<U>& X, const Cursor& c, const int* ids) {
+    if constexpr (APPEND)
+      st.issue_last(X, c.j * CH, c.L, ids, c.cb + c.j + 1 == c.ce ? c.L - 1 : -1,
+                    ap.key + (int64_t)c.b * ap.key_stride, ap.value + (int64_t)c.b * ap.value_stride);
+    else
+      st.issue(X, c.j * CH, c.L, ids);
+  };
+  // After the chunk at c (held in X): if it closes a piece (its sequence's last chunk or the
   // slice's last chunk), write the piece and start the next sequence's state.
-  auto finish = [&](const Cursor& c, const Cursor& next) {
+  auto finish = [&](const Cursor& c, const Cursor& next, const KVRegs<U>& X) {
     if (c.cb + c.j + 1 != c.ce && c.f + 1 != f_end) return;
+    if constexpr (APPEND)
+      if (c.cb + c.j + 1 == c.ce && hw % tiles == 0) {
+        const int jb = (c.L - 1) >> bs_log2;
+        st.store_new(X, c.j * CH, c.L, jb < maxb ? bt_of(c)[jb] : -1, ap.kc, ap.vc);
+      }
     st.fold();
     if (c.cb >= f_begin && c.ce <= f_end) {
       st.store_final(out, (int64_t)c.row * HQ + h0);
@@ -476,37 +538,37 @@ __device__ __forceinline__ void decode_balanced_run(
   int idsA[U], idsB[U];
   Cursor c1 = cursor_next(c0, B, s_cuc, s_len, s_row);
   st.fetch_ids(bt_of(c0), c0.j * CH, c0.L, idsA);
-  st.issue(A, c0.j * CH, c0.L, idsA);
+  iss(A, c0, idsA);
   if (n > 1) st.fetch_ids(bt_of(c1), c1.j * CH, c1.L, idsB);
   for (int k = 0; k < (n - 1) / 2; ++k) {
-    st.issue(Bv, c1.j * CH, c1.L, idsB);
+    iss(Bv, c1, idsB);
     const Cursor c2 = cursor_next(c1, B, s_cuc, s_len, s_row);
     st.fetch_ids(bt_of(c2), c2.j * CH, c2.L, idsA);
     st.compute(A, c0.j * CH, c0.L);
-    finish(c0, c1);
-    st.issue(A, c2.j * CH, c2.L, idsA);
+    finish(c0, c1, A);
+    iss(A, c2, idsA);
     const Cursor c3 = cursor_next(c2, B, s_cuc, s_len, s_row);
     if (c3.f < f_end) st.fetch_ids(bt_of(c3), c3.j * CH, c3.L, idsB);
     st.compute(Bv, c1.j * CH, c1.L);
-    finish(c1, c2);
+    finish(c1, c2, Bv);
     c0 = c2;
     c1 = c3;
   }
   if ((n - 1) & 1) {
-    st.issue(Bv, c1.j * CH, c1.L, idsB);
+    iss(Bv, c1, idsB);
     st.compute(A, c0.j * CH, c0.L);
-    finish(c0, c1);
+    finish(c0, c1, A);
     st.compute(Bv, c1.j * CH, c1.L);
-    finish(c1, c1);
+    finish(c1, c1, Bv);
   } else {
     st.compute(A, c0.j * CH, c0.L);
-    finish(c0, c1);
+    finish(c0, c1, A);
   }
 }
 
 // The whole balanced-split slice for a standalone launch: every wave of the workgroup
 // takes part in the length scan's barrier, then runs its slice.
-template <int D, int ET, int G, bool VARLEN>
+template <int D, int ET, int G, bool VARLEN, bool APPEND = false>
 __device__ __forceinline__ void decode_balanced_body(
     int w, int hw, bool write_cuc, void* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_cuc,
@@ -514,15 +576,16 @@ __device__ __forceinline__ void decode_balanced_body(
     const void* __restrict__ vcache, const int32_t* __restrict__ block_table, int maxb,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int total_q, int B, int num_blocks, int bs_log2, int HQ,
-    int HKV, int group, float scale_log2, int Wt) {
+    int HKV, int group, float scale_log2, int Wt, const AppendRows& ap = AppendRows{}) {
   extern __shared__ int s_mem[];
   if (threadIdx.x < 64)
     balanced_scan<DecodeWave<D, ET, G>::CH, VARLEN>(s_mem, context_lens, cu_q, cu_k, total_q, B,
                                                      [](int, int, int) {});
   __syncthreads();
-  decode_balanced_run<D, ET, G, VARLEN>(s_mem, w, hw, write_cuc, out, ws_acc, ws_m, ws_l, ws_cuc,
-                                        qptr, kcache, vcache, block_table, maxb, B, num_blocks,
-                                        bs_log2, HQ, HKV, group, scale_log2, Wt);
+  decode_balanced_run<D, ET, G, VARLEN, APPEND>(s_mem, w, hw, write_cuc, out, ws_acc, ws_m, ws_l,
+                                                ws_cuc, qptr, kcache, vcache, block_table, maxb, B,
+                                                num_blocks, bs_log2, HQ, HKV, group, scale_log2,
+                                                Wt, ap);
 }
 
 

@@ -20,6 +20,17 @@ int check_launch(const char* what);
 // or pa_set_debug_checks).
 bool debug_checks();
 
+// The new rows of a decode batch (row b is key context_lens[b] - 1 of sequence b) stored to
+// their slots by one launch (pa_store.hip); inputs already checked.
+int launch_store_decode_rows(const void* key, const void* value, int64_t key_stride_bytes,
+                             int64_t value_stride_bytes, void* k_cache, void* v_cache,
+                             const int32_t* block_table, int32_t maxb,
+                             const int32_t* context_lens, int32_t B, int32_t num_blocks,
+                             int32_t block_size, int64_t row_bytes, hipStream_t s);
+// Debug check of those rows' slots (pa_check.cpp): no two sequences' new rows share one.
+int check_append_slots(const int32_t* block_table, int32_t maxb, const int32_t* context_lens,
+                       int32_t B, int32_t num_blocks, int32_t block_size, hipStream_t s);
+
 inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 __host__ __device__ constexpr inline int elt_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }

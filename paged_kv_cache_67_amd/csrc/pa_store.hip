@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void store_kv_paged_kernel(
     int num_blocks, int row_chunks, int64_t row_bytes, int32_t* __restrict__ slots_out) {
   const int bs = 1 << bs_log2;
   for (int b = blockIdx.y; b < num_seqs; b += gridDim.y) {
-    const int q0 = cu_q[b];
-    const int lq = cu_q[b + 1] - q0;
+    const int q0 = cu_q ? cu_q[b] : b;  // no cu_q: one token per sequence (token b)
+    const int lq = cu_q ? cu_q[b + 1] - q0 : 1;
     const int lk = lens_k[b];
     const int32_t* row = block_table + (int64_t)b * maxb;
     const int64_t items = (int64_t)(lq > 0 ? lq : 0) * row_chunks;
@@ -247,6 +247,26 @@ extern "C" int pa_store_kv(const void* key, const void* value, int64_t key_token
                      row_chunks, (int64_t)num_blocks * block_size, row_bytes);
   return check_launch("pa_store_kv");
 }
+
+namespace pa {
+
+// The new rows of a decode batch (row b is key context_lens[b] - 1 of sequence b) into the
+// cache: the fused store's kernel with one token per sequence.  Inputs already checked.
+int launch_store_decode_rows(const void* key, const void* value, int64_t key_stride_bytes,
+                             int64_t value_stride_bytes, void* k_cache, void* v_cache,
+                             const int32_t* block_table, int32_t maxb,
+                             const int32_t* context_lens, int32_t B, int32_t num_blocks,
+                             int32_t block_size, int64_t row_bytes, hipStream_t s) {
+  const int row_chunks = int(row_bytes / 16);
+  const dim3 grid(unsigned((row_chunks + 255) / 256), unsigned(B < 65535 ? B : 65535));
+  hipLaunchKernelGGL(store_kv_paged_kernel, grid, dim3(256), 0, s, (const char*)key,
+                     (const char*)value, key_stride_bytes, value_stride_bytes, (char*)k_cache,
+                     (char*)v_cache, block_table, maxb, nullptr, context_lens, B, B,
+                     __builtin_ctz(block_size), num_blocks, row_chunks, row_bytes, nullptr);
+  return check_launch("store of the new decode rows");
+}
+
+}  // namespace pa
 
 extern "C" int pa_store_kv_paged(const void* key, const void* value, int64_t key_token_stride,
                                  int64_t value_token_stride, void* k_cache, void* v_cache,

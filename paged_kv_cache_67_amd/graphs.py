@@ -7,10 +7,11 @@ steps of 16), copies each step's inputs into the captured fixed buffers and
 replays: a batch of 9 replays the 16-row graph, and the 7 padded rows have
 slot -1 and context length 0, so they write no cache row.  B.5 adds that a
 batch no bucket covers runs eagerly instead of failing.  Both hold here for the
-library's kernels: slot addressing gives -1 for a row with context 0 (the
-scatter skips it), decode gives such a row zeros without reading the cache,
-and the library allocates nothing and never synchronises, so the captured
-launches are the eager ones.
+library's kernels: the step is one pa_decode_append call (store of the new rows
+and decode; for short slices one first pass and a merge), which stores nothing
+for a row with context 0 and gives it zeros without reading the cache, and the
+library allocates nothing and never synchronises, so the captured launches are
+the eager ones.
 
     runner = GraphedDecode(k_cache, v_cache, num_q_heads=16, max_blocks_per_seq=16,
                            max_context_len=4096, scale=1 / 128 ** 0.5, max_batch=256)
@@ -40,7 +41,7 @@ def default_buckets(max_batch):
 
 
 class GraphedDecode:
-    """slot addressing + K/V scatter + decode for one layer, replayed per batch bucket.
+    """slot addressing + K/V store + decode for one layer, replayed per batch bucket.
 
     Buffers are sized for the largest bucket.  ``step`` copies the live rows in,
     marks the rows up to the bucket as padding (context 0) and replays that
@@ -67,8 +68,6 @@ class GraphedDecode:
         self.out = torch.zeros(bmax, num_q_heads, D, dtype=dt, device=dev)
         self.block_table = torch.full((bmax, max_blocks_per_seq), -1, dtype=torch.int32, device=dev)
         self.context_lens = torch.zeros(bmax, dtype=torch.int32, device=dev)
-        self.cu_q = torch.arange(bmax + 1, dtype=torch.int32, device=dev)
-        self.slots = torch.full((bmax,), -1, dtype=torch.int32, device=dev)
         nbytes = pa.pa_decode_workspace_size(bmax, num_q_heads, HKV, D, self.max_context_len, 0)
         self.workspace = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=dev)
         self.graphs = {}
@@ -107,12 +106,11 @@ class GraphedDecode:
         return self.buckets[i] if i < len(self.buckets) else None
 
     def _launch(self, b):
-        pa.pa_store_kv_paged(self.k_new[:b], self.v_new[:b], self.k_cache, self.v_cache,
-                             self.block_table[:b], self.cu_q[:b + 1], self.context_lens[:b], 1,
-                             self.slots[:b])
-        pa.pa_decode(self.out[:b], self.q[:b], self.k_cache, self.v_cache, self.block_table[:b],
-                     self.context_lens[:b], self.scale, max_context_len=self.max_context_len,
-                     partition_size=0, workspace=self.workspace)
+        pa.pa_decode_append(self.out[:b], self.q[:b], self.k_new[:b], self.v_new[:b],
+                            self.k_cache, self.v_cache, self.block_table[:b],
+                            self.context_lens[:b], self.scale,
+                            max_context_len=self.max_context_len, partition_size=0,
+                            workspace=self.workspace)
 
     def capture(self, b):
         """Capture bucket b (the buffers' current rows are run once eagerly first)."""
@@ -129,15 +127,13 @@ class GraphedDecode:
         """The same step launched directly on the caller's tensors (no graph)."""
         n = q.shape[0]
         dev = q.device
-        cu_q = torch.arange(n + 1, dtype=torch.int32, device=dev)
-        pa.pa_store_kv_paged(k_new, v_new, self.k_cache, self.v_cache, block_table, cu_q,
-                             context_lens, 1)
         out = torch.empty_like(q)
         nbytes = pa.pa_decode_workspace_size(n, q.shape[1], self.k_cache.shape[2], q.shape[2],
                                              self.max_context_len, 0)
         ws = torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.float32, device=dev)
-        pa.pa_decode(out, q, self.k_cache, self.v_cache, block_table, context_lens, self.scale,
-                     max_context_len=self.max_context_len, partition_size=0, workspace=ws)
+        pa.pa_decode_append(out, q, k_new, v_new, self.k_cache, self.v_cache, block_table,
+                            context_lens, self.scale, max_context_len=self.max_context_len,
+                            partition_size=0, workspace=ws)
         return out
 
     def inputs(self, n):

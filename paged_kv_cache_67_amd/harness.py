@@ -108,6 +108,16 @@ class DeviceWorkload:
                                 self.cu_q, self.cu_k, w.max_seqlen_q, w.max_seqlen_k, w.scale,
                                 causal=True, stream=stream)
 
+    def attention_append(self, stream=None):
+        """Store of the new rows and decode in one call (pa_decode_append); the cache then
+        holds the new rows as after store_paged()."""
+        w = self.w
+        pa.pa_decode_append(self.out, self.q, self.k_new, self.v_new, self.k_cache, self.v_cache,
+                            self.block_table, self.seq_lens_k, w.scale,
+                            max_context_len=self.max_context_len,
+                            partition_size=self.partition_size, workspace=self.workspace,
+                            stream=stream)
+
     def attention_mixed(self, stream=None):
         """The whole batch in one launch: its one-query sequences take the decode
         path and the others the prefill path (pa_attention_mixed)."""

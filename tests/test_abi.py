@@ -110,6 +110,15 @@ def test_null_and_shape_errors(L):
     assert L.pa_decode_noalloc(None, None, None, None, None, 4, None, 2, 0, 8, 16, 3, 2, 64, 0.1, 0, 0, None) == 2
     assert L.pa_decode_noalloc(None, None, None, None, None, 4, None, 2, 0, 8, 16, 4, 2, 64, 0.1, 1, 0, None) == 1
     assert L.pa_decode_noalloc(None, None, None, None, None, 4, None, 0, 0, 8, 16, 4, 2, 64, 0.1, 1, 0, None) == 0
+    # pa_decode_append(_partitions): pa_decode's checks first; an empty batch is a no-op
+    app = lambda B, hq, d, dt: L.pa_decode_append(
+        None, None, None, None, 128, 128, None, None, None, 4, None, B, 0, 8, 16, hq, 2, d, 0.1, dt,
+        0, None, 0, None)
+    assert app(2, 4, 64, 1) == 1
+    assert app(2, 4, 64, 3) == 3
+    assert app(2, 4, 96, 1) == 3
+    assert app(2, 3, 64, 1) == 2
+    assert app(0, 4, 64, 1) == 0
 
 
 def _gpu_visible():
@@ -152,6 +161,22 @@ def test_alignment_and_workspace_errors(L):
     assert L.pa_decode_noalloc(a, a, a, a, a, 16, a, 512, 4096, 8, 256, 16, 8, 128, 0.1, 1, 16, None) == 5
     assert "scratch" in pk.pa_last_error()
     assert L.pa_decode_noalloc(a, a, a, mis, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, 0, None) == 4
+    # pa_decode_append: the new rows' pointers and strides (bf16 rows of 2 x 64 elements),
+    # then the workspace, all refused before anything is enqueued
+    app = lambda key, kst, vst, part, ws, wsb, out=a: L.pa_decode_append(
+        out, a, key, a, kst, vst, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, part, ws, wsb, None)
+    assert app(None, 128, 128, 0, a, need0) == 1
+    assert app(mis, 128, 128, 0, a, need0) == 4
+    assert app(a, 132, 128, 0, a, need0) == 4       # 264-byte stride: rows not 16-byte aligned
+    assert app(a, 128, 100, 0, a, need0) == 2       # stride shorter than a row
+    assert app(a, 128, 128, 0, a, 16) == 5          # balanced split, workspace too small
+    assert app(a, 128, 128, 16, None, 0) == 5       # fixed partitions without a workspace
+    assert app(a, 128, 128, 0, a, need0, out=None) == 1
+    assert app(a, 128, 128, 0, a, need0, out=mis) == 4
+    appp = lambda part, ws, wsb: L.pa_decode_append_partitions(
+        a, a, a, a, 128, 128, a, a, a, 4, a, 2, 64, 8, 16, 4, 2, 64, 0.1, 1, part, ws, wsb, None)
+    assert appp(-1, a, need) == 5                    # the first pass alone needs a split
+    assert appp(128, a, need) == 3                   # P = 128 does not split 64 keys
 
 
 def test_workspace_size_closed_form(L):
