@@ -282,17 +282,14 @@ def time_graphs(w, dw, args):
     for n in (1, 8, 64, w.num_seqs):
         q, kn, vn = dw.q[:n], dw.k_new[:n], dw.v_new[:n]
         bt, ctx = dw.block_table[:n], dw.seq_lens_k[:n]
-        slots = torch.empty(n, dtype=torch.int32, device="cuda")
-        cu = torch.arange(n + 1, dtype=torch.int32, device="cuda")
         out = torch.empty_like(q)
         nbytes = pk.pa_decode_workspace_size(n, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                              w.max_seqlen_k, 0)
         ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
 
-        def eager():
-            pk.pa_store_kv_paged(kn, vn, dw.k_cache, dw.v_cache, bt, cu, ctx, 1, slots)
-            pk.pa_decode(out, q, dw.k_cache, dw.v_cache, bt, ctx, w.scale,
-                         max_context_len=w.max_seqlen_k, partition_size=0, workspace=ws)
+        def eager():  # the captured step, called directly on the caller's tensors
+            pk.pa_decode_append(out, q, kn, vn, dw.k_cache, dw.v_cache, bt, ctx, w.scale,
+                                max_context_len=w.max_seqlen_k, partition_size=0, workspace=ws)
 
         def graphed():
             runner.step(q, kn, vn, bt, ctx)
