@@ -154,6 +154,22 @@ def test_entry_points_check_before_launch(checks_on):
         pk.pa_store_kv_paged(dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, twin_bt, dw.cu_q,
                              twin_lens, 1, dw.slots_new)
     assert _status(e) == CONTRACT and "written twice" in str(e.value)
+    # pa_decode_append: the decode check first, then no two new rows in one slot
+    with pytest.raises(pk.PAError) as e:
+        pk.pa_decode_append(dw.out, dw.q, dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, bad_bt,
+                            dw.seq_lens_k, w.scale, max_context_len=dw.max_context_len,
+                            workspace=dw.workspace)
+    assert _status(e) == CONTRACT and "block_table[0][1]" in str(e.value), str(e.value)
+    with pytest.raises(pk.PAError) as e:
+        pk.pa_decode_append(dw.out, dw.q, dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, twin_bt,
+                            twin_lens, w.scale, max_context_len=dw.max_context_len,
+                            workspace=dw.workspace)
+    assert _status(e) == CONTRACT and "share slot" in str(e.value), str(e.value)
+    pk.pa_decode_append(dw.out, dw.q, dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, dw.block_table,
+                        dw.seq_lens_k, w.scale, max_context_len=dw.max_context_len,
+                        workspace=dw.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(got, dw.out)
 
     assert pk.pa_set_debug_checks(False)
     try:
