@@ -236,10 +236,15 @@ static int launch_merge(void* out, const DecodePlan& pl, const WsPtrs& w,
   else                                                                                           \
     hipLaunchKernelGGL((merge_kernel<ET, WV>), grid, block, 0, s, out, w.acc, w.m, w.l,          \
                        context_lens, HQ, D, pl.NP, pl.P);
-#define PA_MERGE(ET)            \
-  if (W == 1) {                 \
-    PA_MERGE_W(ET, 1)           \
-  } else if (W == 2) {          \
+#define PA_MERGE(ET)                                                                          \
+  if (W == 1 && pl.mode == DecodePlan::kBalanced) {                                           \
+    hipLaunchKernelGGL((merge_balanced_kernel<ET, false, 1, kMergeHeadsPerWG>),               \
+                       dim3((HQ + kMergeHeadsPerWG - 1) / kMergeHeadsPerWG, B),                \
+                       dim3(64 * kMergeHeadsPerWG), 0, s, out, w.acc, w.m, w.l, w.cuc, nullptr, \
+                       0, B, HQ, D, pl.Wt);                                                    \
+  } else if (W == 1) {                                                                        \
+    PA_MERGE_W(ET, 1)                                                                         \
+  } else if (W == 2) {                                                                        \
     PA_MERGE_W(ET, 2)           \
   } else if (W == 4) {          \
     PA_MERGE_W(ET, 4)           \

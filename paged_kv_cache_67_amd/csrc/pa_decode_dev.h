@@ -593,6 +593,10 @@ __device__ __forceinline__ void decode_balanced_body(
 // loads in flight.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeUnroll = 8;
+// One-wave merges (short rows) run kMergeHeadsPerWG query heads per workgroup: the 256-row
+// Qwen3-0.6B decode's merge dispatches 1024 workgroups instead of 4096 (step 347.4-347.6
+// against 348.4 us; 8 heads gave the same).
+constexpr int kMergeHeadsPerWG = 4;
 // Waves per merge workgroup.  A grid of at most one workgroup per compute unit leaves most
 // of the chip idle, so the widest workgroup costs nothing there, and it is what a row far
 // longer than the rest (which the host cannot see) needs.  A larger grid pays for every
@@ -621,7 +625,7 @@ __device__ __forceinline__ void merge_states(void* __restrict__ out, int64_t row
                                              Idx idx) {
   using E = Elem<ET>;
   constexpr int U = kMergeUnroll;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = W == 1 ? 0 : threadIdx.x >> 6;
   const bool two = D > 64;
   constexpr float kFloor = -1.0e30f;  // finite: e^(kFloor - M) is 0, never NaN
   float M = kFloor, L = 0.0f, A0 = 0.0f, A1 = 0.0f;
@@ -700,13 +704,17 @@ __device__ __forceinline__ void merge_states(void* __restrict__ out, int64_t row
 // the one-query sequences of a varlen batch are decode rows (row cu_q[b]); the
 // others belong to the prefill side and are left alone, and the slice count is the one
 // the first pass stored after its scan (Wt is then unused).
-template <int ET, bool VARLEN, int W>
-__global__ __launch_bounds__(64 * W) void merge_balanced_kernel(
+// HPW (with W = 1): query heads per workgroup, one wave each, so that a batch of short rows
+// dispatches HPW times fewer workgroups.
+template <int ET, bool VARLEN, int W, int HPW = 1>
+__global__ __launch_bounds__(64 * W * HPW) void merge_balanced_kernel(
     void* __restrict__ out, const float* __restrict__ ws_acc, const float* __restrict__ ws_m,
     const float* __restrict__ ws_l, const int32_t* __restrict__ ws_cuc,
     const int32_t* __restrict__ cu_q, int total_q, int B, int HQ, int D, int Wt) {
+  static_assert(HPW == 1 || W == 1, "several heads per workgroup only with one wave each");
   using E = Elem<ET>;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x * HPW + (HPW > 1 ? (int)(threadIdx.x >> 6) : 0), b = blockIdx.y;
+  if (h >= HQ) return;
   int rb = b;
   if constexpr (VARLEN) {
     rb = cu_q[b];
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(64 * W) void merge_balanced_kernel(
   const int64_t row = ((int64_t)rb * HQ + h) * D;
   const int cb = ws_cuc[b], ce = ws_cuc[b + 1];
   if (cb >= ce) {  // no keys: zero row
-    for (int d = threadIdx.x; d < D; d += blockDim.x) E::store(out, row + d, 0.0f);
+    for (int d = threadIdx.x & (64 * W - 1); d < D; d += 64 * W) E::store(out, row + d, 0.0f);
     return;
   }
   const int NC = ws_cuc[B];

@@ -381,17 +381,23 @@ extern "C" int pa_attention_mixed(void* out, const void* q, const void* k_cache,
   hipLaunchKernelGGL((merge_balanced_kernel<ET, true, WV>), mgrid, dim3(64 * WV), 0, s, out, \
                      w.acc, w.m, w.l, w.cuc, cu_seqlens_q, total_q, num_seqs, num_q_heads,  \
                      head_dim, pl.Wt)
+#define PA_MIXED_MERGE1(ET)                                                                  \
+  hipLaunchKernelGGL((merge_balanced_kernel<ET, true, 1, kMergeHeadsPerWG>),                 \
+                     dim3((num_q_heads + kMergeHeadsPerWG - 1) / kMergeHeadsPerWG, num_seqs), \
+                     dim3(64 * kMergeHeadsPerWG), 0, s, out, w.acc, w.m, w.l, w.cuc,          \
+                     cu_seqlens_q, total_q, num_seqs, num_q_heads, head_dim, pl.Wt)
   if (dtype == PA_F16) {
-    if (W == 1) PA_MIXED_MERGE(PA_F16, 1);
+    if (W == 1) PA_MIXED_MERGE1(PA_F16);
     else if (W == 2) PA_MIXED_MERGE(PA_F16, 2);
     else if (W == 4) PA_MIXED_MERGE(PA_F16, 4);
     else PA_MIXED_MERGE(PA_F16, kMergeWaves);
   } else {
-    if (W == 1) PA_MIXED_MERGE(PA_BF16, 1);
+    if (W == 1) PA_MIXED_MERGE1(PA_BF16);
     else if (W == 2) PA_MIXED_MERGE(PA_BF16, 2);
     else if (W == 4) PA_MIXED_MERGE(PA_BF16, 4);
     else PA_MIXED_MERGE(PA_BF16, kMergeWaves);
   }
 #undef PA_MIXED_MERGE
+#undef PA_MIXED_MERGE1
   return check_launch("pa_attention_mixed merge");
 }
