@@ -55,12 +55,32 @@ def _run(w, ctx, partition, two_pass=False, with_workspace=True):
     return dw, out
 
 
-def _check(w, ctx, partition, what, two_pass=False, with_workspace=True):
+def _two_calls(w, ctx, partition):
+    """The same step as pa_store_kv_paged + pa_decode (the results pa_decode_append promises)."""
+    dw = harness.DeviceWorkload(w, "cuda", partition_size=partition, with_workspace=False)
+    dw.load_history()
+    ctx_t = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).cuda()
+    cu = torch.arange(w.num_seqs + 1, dtype=torch.int32, device="cuda")
+    pk.pa_store_kv_paged(dw.k_new, dw.v_new, dw.k_cache, dw.v_cache, dw.block_table, cu, ctx_t, 1)
+    out = torch.full_like(dw.out, float("nan"))
+    max_ctx = max(1, int(np.max(ctx)))
+    nbytes = pk.pa_decode_workspace_size(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                         max_ctx, partition)
+    ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda") if nbytes else None
+    pk.pa_decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_table, ctx_t, w.scale,
+                 max_context_len=max_ctx, partition_size=partition, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(w, ctx, partition, what, two_pass=False, with_workspace=True, bitwise=False):
     dw, out = _run(w, ctx, partition, two_pass, with_workspace)
     k_pool, v_pool, want = _oracle(w, np.asarray(ctx, dtype=np.int32))
     assert bits_equal(harness.from_device(dw.k_cache), k_pool), f"{what}: K pool"
     assert bits_equal(harness.from_device(dw.v_cache), v_pool), f"{what}: V pool"
     assert_close(out_f64(out, w.dtype), want, w.dtype, what)
+    if bitwise:  # and the two calls' rows bit for bit
+        assert torch.equal(out, _two_calls(w, ctx, partition)), f"{what}: differs from two calls"
     return out
 
 
@@ -100,7 +120,7 @@ def test_append_edge_rows(case, partition):
                       num_kv_heads=HKV, head_dim=D, block_size=bs, seq_lens_k=np.maximum(lens, 1),
                       seed=500 + EDGE_CASES.index(case))
     announce(f"pa_decode_append edge rows {case[:5]} partition {partition}")
-    _check(w, lens, partition, f"{case[:5]} p{partition}")
+    _check(w, lens, partition, f"{case[:5]} p{partition}", bitwise=True)
 
 
 @pytest.mark.parametrize("partition", [0, 64])
@@ -123,7 +143,8 @@ def test_append_without_workspace_is_a_single_pass():
 @pytest.mark.parametrize("seed", list(range(16)))
 def test_append_random_shapes(seed):
     """The seeded random decode batches of the decode parity suite (GQA 1-8 or 16, d 64 / 128,
-    block 8-512, batch 1-300 with short, empty and long rows, three dtypes, every split)."""
+    block 8-512, batch 1-300 with short, empty and long rows, three dtypes, every split); the
+    rows also equal store + decode bit for bit."""
     c = _random_decode_case(4000 + seed)
     lens = np.array(c["lens"], dtype=np.int32)
     w = make_workload(name="rand-append", kind="decode", dtype=c["dtype"],
@@ -131,4 +152,4 @@ def test_append_random_shapes(seed):
                       block_size=c["bs"], seq_lens_k=np.maximum(lens, 1), seed=seed)
     announce(f"random append case {seed}: " + str({k: v for k, v in c.items() if k != "lens"}) +
              f" B={len(lens)} max={int(lens.max())}")
-    _check(w, lens, c["P"], str(c))
+    _check(w, lens, c["P"], str(c), bitwise=True)
