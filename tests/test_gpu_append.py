@@ -4,7 +4,8 @@ Against the oracle -- outputs to the dtype's tolerance, both pools bit for bit -
 decode workloads in every split mode, on the head tiles that store with a launch of their
 own (fp16 tiles of 4, 6, 7 or 8 heads), on two head waves per KV head (one of them writes), and
 on the edge rows: a key that
-is the sequence's only one, empty rows (no row stored), keys on block and chunk boundaries.
+is the sequence's only one, empty rows (no row stored), keys on block and chunk boundaries;
+and on both sides of the balanced split's 8192-sequence bound.
 The pools start NaN-poisoned, so a read of the new row's slot before it is written shows.
 """
 
@@ -153,3 +154,18 @@ def test_append_random_shapes(seed):
     announce(f"random append case {seed}: " + str({k: v for k, v in c.items() if k != "lens"}) +
              f" B={len(lens)} max={int(lens.max())}")
     _check(w, lens, c["P"], str(c), bitwise=True)
+
+
+@pytest.mark.parametrize("B", [8192, 8193])
+def test_append_at_the_balanced_batch_bound(B):
+    """Both sides of the balanced split's batch bound: 8192 short sequences take the
+    balanced first pass with the store folded in (many sequences per slice, each ending in
+    it), 8193 take fixed partitions after a store launch.  Pools bit for bit, rows against
+    the oracle and bit for bit against store + pa_decode; empty rows mixed in."""
+    rng = np.random.default_rng(B + 1)
+    lens = rng.integers(0, 40, size=B, endpoint=True).astype(np.int32)
+    w = make_workload(name=f"append-b{B}", kind="decode", dtype="bf16", num_q_heads=14,
+                      num_kv_heads=2, head_dim=64, block_size=16, seq_lens_k=np.maximum(lens, 1),
+                      seed=B % 991)
+    announce(f"pa_decode_append at the balanced batch bound: B={B}")
+    _check(w, lens, 0, f"B={B}", bitwise=True)
