@@ -349,6 +349,9 @@ PREFILL_CASES = [
     # block tables longer than the kernel's LDS copy (2048 entries): the window slides
     (2, 1, 64, 8, [40000, 300], [40, 100]),
     (8, 2, 128, 8, [18000], [32]),
+    # a long prompt with no cached prefix beside an empty chunk (Lq = 0: no rows)
+    (16, 8, 128, 256, [3000, 500, 64], [3000, 0, 64]),
+    (16, 8, 128, 256, [1300, 40, 700], [0, 40, 700]),  # the first sequence has no rows
 ]
 
 
